@@ -1,0 +1,55 @@
+"""Size and work accounting for the selective mixer core (host-side arithmetic only).
+
+State: each retained channel carries m complex mode states of P values, i.e.
+2 K_T m P real entries per spectral layer (ESSH paper, Sec. 4.3), kept in fp32.
+
+Algorithmic work is what the method must move or compute, excluding any
+workspace, re-reads or padding of an implementation:
+
+  prefill, per (token, retained channel):
+      bytes = P*s_io (v) + P*s_io (y) + 4 (clock) + 2*s_io (write and read gate)
+      flops = 10*m*P + 2*P   (per mode and value: complex state update 7,
+                              readout 3; per value: write-gate and read-gate
+                              products)
+    plus, per call, the mode tables (16 B per retained (k, j): rho, theta, c)
+    and the final state if it is written (8 B per retained (b, k, j, p)).
+
+  decode, per (layer, batch row, retained channel):
+      bytes = 2 * 8*m*P (state read + written, fp32 complex)
+              + P*s_io (v) + P*s_io (y) + 4 + 2*s_io (clock, gates)
+              + 16*m (mode tables)
+      flops = 10*m*P + 2*P
+"""
+from __future__ import annotations
+
+IO_BYTES = {"f32": 4, "bf16": 2}
+
+
+def state_bytes(n_layers: int, B: int, K: int, m: int, P: int) -> int:
+    """Bytes of fp32 recurrent state for K retained channels over n_layers layers."""
+    return 2 * n_layers * B * K * m * P * 4
+
+
+def prefill_bytes(B: int, L: int, K_T: int, m: int, P: int, io: str,
+                  write_state: bool = False, per_mode: bool = False) -> int:
+    s = IO_BYTES[io]
+    nc = m if per_mode else 1
+    per_tok = 2 * P * s + nc * (4 + 2 * s)
+    total = B * L * K_T * per_tok + K_T * m * 16
+    if write_state:
+        total += state_bytes(1, B, K_T, m, P)
+    return total
+
+
+def prefill_flops(B: int, L: int, K_T: int, m: int, P: int) -> int:
+    return B * L * K_T * (10 * m * P + 2 * P)
+
+
+def decode_bytes(n_layers: int, B: int, K_T: int, m: int, P: int, io: str) -> int:
+    s = IO_BYTES[io]
+    per = 2 * 8 * m * P + 2 * P * s + 4 + 2 * s + 16 * m
+    return n_layers * B * K_T * per
+
+
+def decode_flops(n_layers: int, B: int, K_T: int, m: int, P: int) -> int:
+    return n_layers * B * K_T * (10 * m * P + 2 * P)
