@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective spectral mixer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one chunked prefill call over the 370M-class mixer-layer workload
+(B=8, L=2048, K=24, m=4, P=64, Lc=64, bf16 v/gates, fp32 clock and state),
+full tier K_T=24, inputs resident in HBM.  ``value`` is tokens per second
+(B*L per step).  The same JSON line also carries
+  * roofline: algorithmic bytes of one prefill launch / its average duration
+    (HIP events around each launch on the launch stream) against 8 TB/s;
+  * cpu_baseline: the CPU oracle (float32 build, OpenMP) on the same workload;
+  * decode: the 24-layer batch-one decode workload (K=32, m=8, P=128, K_T=32),
+    1024 steps replayed from a HIP graph, us/step and kernel roofline;
+  * extra: tier sweeps of the three prefill workloads.
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+SLEEP_CYCLES = 200_000_000
+METRIC = "selective spectral scan prefill tokens/s + decode µs/step, % of HBM roofline"
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def to_dev(x):
+    import numpy as np
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def time_launches(fn, steps, warmup):
+    """Returns (ms per step over the whole timed region, mean ms per launch from per-launch events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # Keep the GPU busy while the host enqueues the timed launches, so that the
+    # events measure back-to-back GPU execution and not host submission speed.
+    torch.cuda._sleep(SLEEP_CYCLES)
+    t0.record(s)
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    t1.record(s)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    return total, statistics.mean(per), statistics.median(per)
+
+
+_CACHE = {}
+
+
+def workload_inputs(widx):
+    from selective_spectral_ssm_amd import inputs as I
+    if widx not in _CACHE:
+        _CACHE.clear()
+        w = I.workload(widx)
+        inp = I.make_prefill_inputs(w)
+        d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
+        _CACHE[widx] = (w, inp, d)
+    return _CACHE[widx]
+
+
+def prefill_case(widx, K_T, steps, warmup):
+    from selective_spectral_ssm_amd import essh, sizes
+    w, inp, d = workload_inputs(widx)
+    call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                        K_T=K_T, Lc=w.Lc, want_state=True)
+    ms_step, ms_launch, ms_med = time_launches(call.run, steps, warmup)
+    nbytes = sizes.prefill_bytes(w.B, w.L, K_T, w.m, w.P, w.io, write_state=True)
+    return dict(workload=w.name, K_T=K_T, ms_per_step=ms_step, us_per_launch=ms_launch * 1e3,
+                us_per_launch_median=ms_med * 1e3,
+                tokens_per_s=w.B * w.L / (ms_step * 1e-3),
+                kernel_tokens_per_s=w.B * w.L / (ms_launch * 1e-3),
+                alg_bytes=nbytes, achieved_GBs=nbytes / (ms_launch * 1e-3) / 1e9), w, inp
+
+
+def decode_case(K_T, n_steps=1024, reps=3, context=2048):
+    import torch
+    from selective_spectral_ssm_amd import essh, inputs as I, sizes
+    w = I.workload(3)
+    log(f"decode: drawing inputs ({w.layers} layers, context {context}, {n_steps} steps)")
+    dec = I.make_decode_inputs(w, n_steps=n_steps, context=context)
+    NL = w.layers
+    rho, theta, c = to_dev(dec["rho"]), to_dev(dec["theta"]), to_dev(dec["c"])
+    state = torch.zeros((NL, 1, w.K, w.m, 2, w.P), device="cuda")
+    for l in range(NL):
+        _, st = essh.prefill(to_dev(dec["ctx_v"][l]), to_dev(dec["ctx_delta"][l]), to_dev(dec["ctx_g_w"][l]),
+                             to_dev(dec["ctx_g_r"][l]), rho[l], theta[l], c[l], K_T=K_T, Lc=64)
+        state[l] = st
+    sv, sd, sgw, sgr = (to_dev(dec[k]) for k in ("step_v", "step_delta", "step_g_w", "step_g_r"))
+    y = torch.empty((n_steps, NL, 1, w.K, w.P), dtype=torch.bfloat16, device="cuda")
+    dims = essh.make_dims(1, 1, w.K, w.m, w.P, K_T, 0, False, "bf16")
+    state0 = state.clone()
+
+    def step(s):
+        rc = essh.essh_mixer_decode_step(NL, dims, sv[s], sd[s], sgw[s], sgr[s], rho, theta, c, state, y[s])
+        assert rc == 0
+
+    # kernel duration: HIP events around each launch (eager)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    for s in range(32):
+        step(s)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    torch.cuda._sleep(SLEEP_CYCLES)   # GPU busy while the host enqueues (see time_launches)
+    for s in range(n_steps):
+        ev[s][0].record(cur)
+        step(s)
+        ev[s][1].record(cur)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    # whole-step wall time: the 1024-step loop captured once in a HIP graph, replayed
+    state.copy_(state0)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step(0)                      # warm the capture stream
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for s in range(n_steps):
+            step(s)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e6 / n_steps)
+    nbytes = sizes.decode_bytes(NL, 1, K_T, w.m, w.P, "bf16")
+    kmean = statistics.mean(per)
+    return dict(workload=w.name, layers=NL, K_T=K_T, steps=n_steps,
+                us_per_step_graph=statistics.median(times), us_per_step_graph_all=times,
+                us_per_kernel_mean=kmean, us_per_kernel_median=statistics.median(per),
+                alg_bytes_per_step=nbytes, achieved_GBs=nbytes / (kmean * 1e-6) / 1e9,
+                frac_of_hbm_peak=nbytes / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+
+def cpu_baseline(inp, w, K_T, budget_s=10.0):
+    import numpy as np
+    import oracle
+    from selective_spectral_ssm_amd.inputs import as_f64
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    nthreads = max(1, min(nthreads, 16))
+    x = dict(v=as_f64(inp["v"], w.io).astype(np.float32), delta=inp["delta"],
+             g_w=as_f64(inp["g_w"], w.io).astype(np.float32), g_r=as_f64(inp["g_r"], w.io).astype(np.float32),
+             rho=inp["rho"], theta=inp["theta"], c=inp["c"])
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 5 and (time.perf_counter() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        oracle.prefill_f32(**x, K_T=K_T, nthreads=nthreads)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return dict(value=w.B * w.L / med, unit="tokens/s", cores=oracle.threads_used("f32"), kind="oracle",
+                sample=f"whole {w.name} workload (B={w.B}, L={w.L}, K_T={K_T}), float32 oracle build, "
+                       f"median of {len(times)} runs", seconds_per_run=med)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the tier sweeps")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_spectral_ssm_amd import essh, sizes
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    essh.lib()   # fail loudly if the HIP library is not built
+
+    log("prefill: mixer370m_prefill K_T=24")
+    main_res, w, inp = prefill_case(1, 24, args.steps, args.warmup)
+    res = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "K": w.K, "K_T": 24, "m": w.m, "P": w.P,
+                   "Lc": w.Lc, "io": w.io, "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel",
+                     "achieved": main_res["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": main_res["achieved_GBs"] / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "alg_bytes_per_launch": main_res["alg_bytes"],
+                     "us_per_launch": main_res["us_per_launch"]},
+    }
+    if not args.no_decode:
+        log("decode: 24 layers K_T=32")
+        res["decode"] = decode_case(32)
+    if not args.no_extra:
+        extra = []
+        for widx, tiers in ((1, (6, 12, 18)), (2, (8, 16, 24, 32)), (4, (6, 12, 18, 24))):
+            for kt in tiers:
+                log(f"tier sweep: workload {widx} K_T={kt}")
+                r, _, _ = prefill_case(widx, kt, max(10, args.steps // 4), 5)
+                extra.append({k: r[k] for k in ("workload", "K_T", "us_per_launch", "kernel_tokens_per_s",
+                                                "achieved_GBs")})
+                extra[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
+        res["prefill_tiers"] = extra
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(inp, w, 24)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * essh.h -- C ABI of the MI355X (gfx950) selective spectral mixer core.
+ *
+ * The method is the selective spectral mixer of "Elastic Selective Spectral
+ * Hybrids for Train-Once, Export-Many Budgeted Inference" (ESSH).  Each
+ * retained spectral channel k < K_T is a bank of m damped-rotation modes:
+ * a complex diagonal recurrence whose per-step decay is set by a
+ * token-dependent clock, with a write gate on the injected channel value and
+ * a read gate on the readout (Sec. 4.1, Eq. 5; App. B, Eq. 9).  In complex
+ * form (App. B.1: a damped rotation rho R(theta) acting on a 2-vector is
+ * multiplication by rho e^{i theta}, injection along e_1 adds to the real
+ * part, reading with (kc, -ks) is Re(c h) with c = kc + i ks):
+ *
+ *   lambda_kj(t) = rho_kj * exp(-delta(t)) * e^{i theta_kj}
+ *   h_kj(t)      = lambda_kj(t) * h_kj(t-1) + g_w(t) * v_k(t)       (per value p)
+ *   y_k(t)       = sum_j g_r(t) * Re(c_kj * h_kj(t))                 (the core output z^core)
+ *
+ * Channels k >= K_T are never read, computed or written (tier truncation,
+ * App. C.4 and D.2; Sec. 4.3 "without evaluating discarded channels").
+ *
+ * Conventions shared by every entry point
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the
+ *     library keeps no reference after the call returns and holds no global
+ *     state, so calls are re-entrant.  Work is enqueued on `stream`
+ *     (a hipStream_t; 0 is the null stream) and the call returns without
+ *     waiting.  Errors detected on the host are returned synchronously and no
+ *     work is enqueued; errors of device execution surface at the caller's
+ *     next synchronisation of the stream, as for any HIP launch.
+ *   - Arrays are dense and row-major.  Shapes use the fields of essh_dims:
+ *       v, y            [B, L, K, P]          io dtype
+ *       delta           [B, L, K]   (or [B, L, K, m] if ctrl_per_mode) fp32, >= 0
+ *       g_w, g_r        [B, L, K]   (or [B, L, K, m] if ctrl_per_mode) io dtype
+ *       rho, theta      [K, m]                fp32, 0 < rho < 1
+ *       c               [K, m, 2]             fp32, (re, im) = (kc, ks)
+ *       state           [B, K, m, 2, P]       fp32, real plane then imaginary plane
+ *     The channel stride of every array is the full K even when K_T < K.
+ *   - Clock and gate values are post-activation: the kernels apply neither
+ *     softplus nor sigmoid (App. C.2 defines those projections upstream).
+ *   - v, y, g_w, g_r, delta and state must be 16-byte aligned; rho, theta, c
+ *     4-byte aligned.  P * sizeof(io dtype) must be a multiple of 16 bytes.
+ */
+#ifndef ESSH_H
+#define ESSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ESSH_OK = 0,
+    ESSH_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, K_T outside [1, K] */
+    ESSH_ERR_UNSUPPORTED = -2,   /* m, P, Lc or dtype outside the compiled set */
+    ESSH_ERR_WORKSPACE = -3,     /* workspace missing or smaller than essh_prefill_workspace_bytes() */
+    ESSH_ERR_HIP = -4            /* a HIP launch or query failed on the host side */
+} essh_status;
+
+typedef enum { ESSH_F32 = 0, ESSH_BF16 = 1 } essh_dtype;
+
+typedef struct {
+    int32_t B;             /* batch rows, >= 0 (0: nothing to do)                          */
+    int32_t L;             /* positions per call, >= 0 (decode ignores it)                 */
+    int32_t K;             /* full channel count; channel stride of every [.., K, ..] array */
+    int32_t m;             /* modes per channel: 1, 2, 4 or 8                              */
+    int32_t P;             /* values per channel: 16, 32, 64 or 128                         */
+    int32_t K_T;           /* retained tier, 1 <= K_T <= K                                 */
+    int32_t Lc;            /* prefill chunk length: 32, 64 or 128; 0 selects 64 (Sec. 4.3 Q=64) */
+    int32_t ctrl_per_mode; /* 0: delta/g_w/g_r per channel [B,L,K]; 1: per mode [B,L,K,m] (Eq. 5) */
+    int32_t io_dtype;      /* essh_dtype of v, g_w, g_r and y; delta, tables and state are fp32 */
+} essh_dims;
+
+/* ABI version of this header (major * 100 + minor). */
+#define ESSH_ABI_VERSION 100
+int32_t essh_abi_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* essh_status_string(essh_status status);
+
+/*
+ * essh_state_init -- zero the recurrent mode state, H(0) = 0 (Eq. 5).
+ *   state     [n_layers, B, K, m, 2, P] fp32, written (all K channels).
+ *   n_layers  >= 1; use 1 for a single mixer.
+ * Uses a fill kernel (no hipMemset), so it may be captured in a HIP graph.
+ * Errors: ESSH_ERR_INVALID_ARG for a null/misaligned state or bad sizes.
+ */
+essh_status essh_state_init(float* state, int32_t n_layers, const essh_dims* d, hipStream_t stream);
+
+/*
+ * essh_prefill_workspace_bytes -- device workspace that essh_mixer_prefill
+ * needs for these dims (0 if none).  Returns 0 for invalid dims as well;
+ * essh_mixer_prefill reports those.
+ */
+size_t essh_prefill_workspace_bytes(const essh_dims* d);
+
+/*
+ * essh_mixer_prefill -- the chunked parallel scan (Sec. 4.3, Fig. 2A).
+ *
+ * Runs the recurrence above over positions 0..L-1 of every batch row for the
+ * retained channels k < K_T and writes y for those channels.  Within a chunk
+ * of Lc positions the source-to-target contributions are evaluated as a
+ * matrix product (Sec. 4.3, the within-chunk matrix G_k); only the 2 m P
+ * mode-state entries of a channel are carried from chunk to chunk (Eq. 6
+ * gives the closed-form transition product that makes this exact).
+ *
+ *   v, delta, g_w, g_r   inputs, layouts above (read only for k < K_T)
+ *   rho, theta, c        mode tables [K, m] / [K, m, 2]
+ *   state_in             [B, K, m, 2, P] state entering position 0, or NULL for H = 0
+ *   state_out            [B, K, m, 2, P] state after position L-1, or NULL;
+ *                        may alias state_in.  Channels k >= K_T untouched.
+ *   y                    [B, L, K, P] output; channels k >= K_T untouched.
+ *   workspace            device scratch of at least essh_prefill_workspace_bytes(d)
+ *                        bytes (may be NULL if that is 0); 256-byte aligned.
+ *   stream               HIP stream to enqueue on.
+ * y must not overlap any input.  Results do not depend on Lc beyond rounding.
+ */
+essh_status essh_mixer_prefill(const essh_dims* d,
+                               const void* v, const float* delta, const void* g_w, const void* g_r,
+                               const float* rho, const float* theta, const float* c,
+                               const float* state_in, float* state_out, void* y,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * essh_mixer_decode_step -- one token through n_layers independent mixers
+ * (the fused recurrent decode of Sec. 4.3 / Sec. 5.3: state update and
+ * readout in one kernel, the state read once and written once, discarded
+ * channels skipped).
+ *
+ *   n_layers             >= 1 independent mixers updated by one launch
+ *   d                    dims of one mixer (L is ignored; Lc ignored)
+ *   v                    [n_layers, B, K, P] io dtype
+ *   delta                [n_layers, B, K] (or [n_layers, B, K, m]) fp32
+ *   g_w, g_r             [n_layers, B, K] (or [n_layers, B, K, m]) io dtype
+ *   rho, theta           [n_layers, K, m] fp32;  c [n_layers, K, m, 2] fp32
+ *   state                [n_layers, B, K, m, 2, P] fp32, updated in place (k < K_T only)
+ *   y                    [n_layers, B, K, P] io dtype; channels k >= K_T untouched
+ */
+essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
+                                   const void* v, const float* delta, const void* g_w, const void* g_r,
+                                   const float* rho, const float* theta, const float* c,
+                                   float* state, void* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ESSH_H */

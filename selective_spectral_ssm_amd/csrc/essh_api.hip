@@ -1,0 +1,150 @@
+// essh_api.hip -- the extern "C" entry points of libessh (declared in include/essh.h).
+//
+// Host-side validation and dispatch only; every arithmetic step runs in the
+// HIP kernels of prefill_chunk.hip, prefill_seq.hip and decode.hip.
+#include <stdint.h>
+
+#include "essh_internal.h"
+
+using namespace essh;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int effective_lc(const essh_dims* d) { return d->Lc == 0 ? 64 : d->Lc; }
+
+essh_status check_dims(const essh_dims* d, bool need_L) {
+    if (!d) return ESSH_ERR_INVALID_ARG;
+    if (d->B < 0 || (need_L && d->L < 0) || d->K < 1) return ESSH_ERR_INVALID_ARG;
+    if (d->K_T < 1 || d->K_T > d->K) return ESSH_ERR_INVALID_ARG;
+    if (d->ctrl_per_mode != 0 && d->ctrl_per_mode != 1) return ESSH_ERR_INVALID_ARG;
+    if (d->io_dtype != ESSH_F32 && d->io_dtype != ESSH_BF16) return ESSH_ERR_UNSUPPORTED;
+    if (!(d->m == 1 || d->m == 2 || d->m == 4 || d->m == 8)) return ESSH_ERR_UNSUPPORTED;
+    if (!(d->P == 16 || d->P == 32 || d->P == 64 || d->P == 128)) return ESSH_ERR_UNSUPPORTED;
+    if (need_L && !(d->Lc == 0 || d->Lc == 32 || d->Lc == 64 || d->Lc == 128)) return ESSH_ERR_UNSUPPORTED;
+    // sizes must stay within 32-bit work-item counts used by the launchers
+    const long long lanes = (long long)d->B * d->K * d->P;
+    if (lanes > (1LL << 30)) return ESSH_ERR_UNSUPPORTED;
+    return ESSH_OK;
+}
+
+essh_status from_hip(hipError_t e) { return e == hipSuccess ? ESSH_OK : ESSH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t essh_abi_version(void) { return ESSH_ABI_VERSION; }
+
+const char* essh_status_string(essh_status s) {
+    switch (s) {
+        case ESSH_OK: return "ESSH_OK";
+        case ESSH_ERR_INVALID_ARG: return "ESSH_ERR_INVALID_ARG: null or misaligned pointer, or a size out of range";
+        case ESSH_ERR_UNSUPPORTED: return "ESSH_ERR_UNSUPPORTED: m, P, Lc or dtype outside the compiled set";
+        case ESSH_ERR_WORKSPACE: return "ESSH_ERR_WORKSPACE: workspace missing or too small";
+        case ESSH_ERR_HIP: return "ESSH_ERR_HIP: a HIP launch failed";
+        default: return "ESSH: unknown status";
+    }
+}
+
+essh_status essh_state_init(float* state, int32_t n_layers, const essh_dims* d, hipStream_t stream) {
+    essh_status st = check_dims(d, false);
+    if (st != ESSH_OK) return st;
+    if (n_layers < 1 || !state || !aligned(state, 16)) return ESSH_ERR_INVALID_ARG;
+    const size_t n = (size_t)n_layers * d->B * d->K * d->m * 2 * d->P;
+    return from_hip(launch_fill_zero(state, n, stream));
+}
+
+size_t essh_prefill_workspace_bytes(const essh_dims* d) {
+    if (check_dims(d, true) != ESSH_OK) return 0;
+    const int lc = effective_lc(d);
+    if (!chunked_supported(d->m, d->P, lc, d->io_dtype, d->ctrl_per_mode)) return 0;
+    return chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc);
+}
+
+essh_status essh_mixer_prefill(const essh_dims* d,
+                               const void* v, const float* delta, const void* g_w, const void* g_r,
+                               const float* rho, const float* theta, const float* c,
+                               const float* state_in, float* state_out, void* y,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    essh_status st = check_dims(d, true);
+    if (st != ESSH_OK) return st;
+    const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
+    if (!v || !delta || !g_w || !g_r || !rho || !theta || !c || !y) return ESSH_ERR_INVALID_ARG;
+    if (!aligned(v, 16) || !aligned(y, 16) || !aligned(delta, 4) || !aligned(g_w, io) || !aligned(g_r, io) ||
+        !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4))
+        return ESSH_ERR_INVALID_ARG;
+    if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return ESSH_ERR_INVALID_ARG;
+    if ((d->P * io) % 16 != 0) return ESSH_ERR_UNSUPPORTED;
+
+    const int lc = effective_lc(d);
+    const bool chunked = chunked_supported(d->m, d->P, lc, d->io_dtype, d->ctrl_per_mode);
+    const size_t need = chunked ? chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ESSH_ERR_WORKSPACE;
+
+    if (d->B == 0) return ESSH_OK;
+    if (d->L == 0) {
+        // no positions: the state passes through unchanged
+        if (state_out) return from_hip(launch_copy_state(state_in, state_out, d->B, d->K, d->K_T, d->m, d->P, stream));
+        return ESSH_OK;
+    }
+
+    PrefillArgs a{};
+    a.B = d->B;
+    a.L = d->L;
+    a.K = d->K;
+    a.K_T = d->K_T;
+    a.Lc = lc;
+    a.per_mode = d->ctrl_per_mode;
+    a.v = v;
+    a.delta = delta;
+    a.g_w = g_w;
+    a.g_r = g_r;
+    a.rho = rho;
+    a.theta = theta;
+    a.c = c;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    hipError_t e = chunked ? launch_prefill_chunked(a, d->m, d->P, stream)
+                           : launch_prefill_sequential(a, d->m, d->P, d->io_dtype, stream);
+    return from_hip(e);
+}
+
+essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
+                                   const void* v, const float* delta, const void* g_w, const void* g_r,
+                                   const float* rho, const float* theta, const float* c,
+                                   float* state, void* y, hipStream_t stream) {
+    essh_status st = check_dims(d, false);
+    if (st != ESSH_OK) return st;
+    if (n_layers < 1) return ESSH_ERR_INVALID_ARG;
+    const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
+    if (!v || !delta || !g_w || !g_r || !rho || !theta || !c || !state || !y) return ESSH_ERR_INVALID_ARG;
+    if (!aligned(v, 16) || !aligned(y, 16) || !aligned(state, 16) || !aligned(delta, 4) || !aligned(g_w, io) ||
+        !aligned(g_r, io) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4))
+        return ESSH_ERR_INVALID_ARG;
+    if ((long long)n_layers * d->B * d->K * d->P > (1LL << 30)) return ESSH_ERR_UNSUPPORTED;
+    if (d->B == 0) return ESSH_OK;
+
+    DecodeArgs a{};
+    a.n_layers = n_layers;
+    a.B = d->B;
+    a.K = d->K;
+    a.K_T = d->K_T;
+    a.per_mode = d->ctrl_per_mode;
+    a.v = v;
+    a.delta = delta;
+    a.g_w = g_w;
+    a.g_r = g_r;
+    a.rho = rho;
+    a.theta = theta;
+    a.c = c;
+    a.state = state;
+    a.y = y;
+    return from_hip(launch_decode(a, d->m, d->P, d->io_dtype, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+"""The C ABI library: it loads, exports what include/essh.h declares, and rejects bad
+arguments on the host before anything is launched (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_spectral_ssm_amd import essh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "essh.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(essh.LIB_PATH):
+        from selective_spectral_ssm_amd import build
+        build.build(verbose=False)
+    return essh.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(essh_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_set():
+    assert declared_functions() == sorted(essh.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libessh.so does not export {name}"
+    assert lib.essh_abi_version() == 100
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert essh.status_string(code).startswith("ESSH_")
+
+
+FAKE = 0x10000          # 16-byte-aligned stand-in address; never dereferenced on these error paths
+
+
+def _call(dims, **over):
+    p = {k: FAKE for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c", "y")}
+    p.update(over)
+    lib = essh.lib()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.essh_mixer_prefill(ctypes.byref(dims), vp(p["v"]), vp(p["delta"]), vp(p["g_w"]), vp(p["g_r"]),
+                                  vp(p["rho"]), vp(p["theta"]), vp(p["c"]), None, None, vp(p["y"]),
+                                  None, 0, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("K_T", 0, essh.ESSH_ERR_INVALID_ARG),
+    ("K_T", 25, essh.ESSH_ERR_INVALID_ARG),
+    ("K", 0, essh.ESSH_ERR_INVALID_ARG),
+    ("B", -1, essh.ESSH_ERR_INVALID_ARG),
+    ("L", -5, essh.ESSH_ERR_INVALID_ARG),
+    ("m", 3, essh.ESSH_ERR_UNSUPPORTED),
+    ("m", 16, essh.ESSH_ERR_UNSUPPORTED),
+    ("P", 48, essh.ESSH_ERR_UNSUPPORTED),
+    ("P", 256, essh.ESSH_ERR_UNSUPPORTED),
+    ("Lc", 16, essh.ESSH_ERR_UNSUPPORTED),
+    ("io_dtype", 7, essh.ESSH_ERR_UNSUPPORTED),
+    ("ctrl_per_mode", 2, essh.ESSH_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_dims(lib, field, value, code):
+    d = essh.make_dims(8, 2048, 24, 4, 64, 24, 64)
+    setattr(d, field, value)
+    assert _call(d) == code
+
+
+@pytest.mark.parametrize("which", ["v", "delta", "g_w", "g_r", "rho", "theta", "c", "y"])
+def test_prefill_rejects_null_pointers(lib, which):
+    d = essh.make_dims(8, 2048, 24, 4, 64, 24, 64)
+    assert _call(d, **{which: None}) == essh.ESSH_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which,addr", [("v", FAKE + 2), ("y", FAKE + 8), ("delta", FAKE + 2), ("g_w", FAKE + 1)])
+def test_prefill_rejects_misaligned(lib, which, addr):
+    d = essh.make_dims(8, 2048, 24, 4, 64, 24, 64)
+    assert _call(d, **{which: addr}) == essh.ESSH_ERR_INVALID_ARG
+
+
+def test_decode_and_state_init_reject_bad_args(lib):
+    d = essh.make_dims(1, 1, 32, 8, 128, 33, 0)
+    f = ctypes.c_void_p(FAKE)
+    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 9), None) == essh.ESSH_ERR_INVALID_ARG
+    d.K_T = 32
+    assert lib.essh_mixer_decode_step(0, ctypes.byref(d), *([f] * 9), None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 8), None, None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_state_init(None, 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_state_init(ctypes.c_void_p(FAKE + 4), 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_prefill(None, *([f] * 11), 0, None) == essh.ESSH_ERR_INVALID_ARG
+
+
+def test_workspace_query_is_total(lib):
+    for args in [(8, 2048, 24, 4, 64, 24, 64), (16, 2048, 32, 8, 128, 8, 64), (1, 131072, 24, 4, 64, 6, 128)]:
+        d = essh.make_dims(*args)
+        assert essh.essh_prefill_workspace_bytes(d) >= 0
+    d = essh.make_dims(8, 2048, 24, 3, 64, 24, 64)   # unsupported m -> 0
+    assert essh.essh_prefill_workspace_bytes(d) == 0

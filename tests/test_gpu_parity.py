@@ -1,0 +1,314 @@
+"""GPU path against the CPU oracle, element by element, through the C ABI (needs an MI355X).
+
+Tolerances: 1e-4 for fp32 inputs and 2e-2 for bf16 inputs with fp32 state,
+as a per-(batch row, channel) normalised maximum error (tests/gpu_util.py).
+Inputs are the seeded synthetic workloads of selective_spectral_ssm_amd.inputs.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from selective_spectral_ssm_amd import inputs as I
+from tests.gpu_util import TOL, block_err, device_inputs, oracle_inputs, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg: str):
+    sys.__stderr__.write(f"[gpu-test] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def _essh():
+    from selective_spectral_ssm_amd import essh
+    return essh
+
+
+def run_gpu_prefill(inp, K_T, Lc=0, state_in=None, y_init=None):
+    import torch
+    essh = _essh()
+    d = device_inputs(inp)
+    s_in = None if state_in is None else to_dev(np.ascontiguousarray(state_in, np.float32))
+    y = None if y_init is None else y_init
+    y, st = essh.prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                         K_T=K_T, Lc=Lc, state_in=s_in, y=y)
+    torch.cuda.synchronize()
+    return y, st
+
+
+def check_prefill(name, inp, K_T, Lc=0, state_in=None):
+    log(f"{name}: prefill K_T={K_T} Lc={Lc} shape={inp['v'].shape} io={inp['io']}")
+    y, st = run_gpu_prefill(inp, K_T, Lc, state_in)
+    ox = oracle_inputs(inp)
+    y_ref, s_ref = oracle.prefill(**ox, K_T=K_T, state_in=state_in)
+    tol = TOL[inp["io"]]
+    ey = block_err(to_host_f64(y)[:, :, :K_T], y_ref[:, :, :K_T], chan_axis=2)
+    es = block_err(to_host_f64(st)[:, :K_T], s_ref[:, :K_T], chan_axis=1)
+    log(f"{name}: y err {ey:.3e}, state err {es:.3e} (tol {tol:g})")
+    assert ey <= tol, f"{name} K_T={K_T}: y error {ey:.3e} > {tol}"
+    assert es <= tol, f"{name} K_T={K_T}: state error {es:.3e} > {tol}"
+    return ey, es
+
+
+# reduced shapes of the five workloads: several chunks and a ragged tail each
+REDUCED = [
+    ("tiny_f32", 0, {}, (8, 3), 0),
+    ("mixer370m_ragged", 1, dict(B=2, L=300), (6, 12, 24), 64),
+    ("mixer1p5b_ragged", 2, dict(B=2, L=200), (8, 32), 64),
+    ("dna_ragged_lc128", 4, dict(L=1000), (6, 24), 128),
+    ("mixer1p5b_lc32", 2, dict(B=1, L=161, K=4), (4,), 32),
+    ("mixer370m_lc128", 1, dict(B=1, L=333, K=4), (3,), 128),
+    ("short_single_partial_chunk", 1, dict(B=3, L=17, K=3), (3,), 64),
+    ("one_position", 2, dict(B=2, L=1, K=2), (2,), 64),
+    ("m1_p16", 1, dict(B=2, L=130, K=3, m=1, P=16), (3,), 64),
+    ("m2_p32", 1, dict(B=2, L=130, K=3, m=2, P=32), (2,), 64),
+    ("m8_p64", 1, dict(B=2, L=150, K=3, m=8, P=64), (3,), 64),
+    ("bf16_p128_m4", 2, dict(B=1, L=129, K=2, m=4), (2,), 64),
+]
+
+
+@pytest.mark.parametrize("name,widx,over,tiers,Lc", REDUCED, ids=[r[0] for r in REDUCED])
+def test_prefill_reduced(name, widx, over, tiers, Lc):
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w)
+    for K_T in tiers:
+        check_prefill(name, inp, K_T, Lc)
+
+
+def test_prefill_state_in_out():
+    w = I.workload(2, B=2, L=150, K=4)
+    inp = I.make_prefill_inputs(w)
+    rng = np.random.default_rng(99)
+    s0 = rng.normal(0, 3.0, size=(2, 4, w.m, 2, w.P)).astype(np.float32)
+    check_prefill("state_in_bf16", inp, 4, 64, state_in=s0)
+    w0 = I.workload(0, L=100)
+    inp0 = I.make_prefill_inputs(w0)
+    s0 = rng.normal(0, 3.0, size=(1, w0.K, w0.m, 2, w0.P)).astype(np.float32)
+    check_prefill("state_in_f32", inp0, w0.K, 0, state_in=s0)
+
+
+def test_prefill_per_mode_controls():
+    for widx, over in ((0, dict(L=90)), (1, dict(B=1, L=70, K=3))):
+        w = I.workload(widx, **over)
+        inp = I.make_prefill_inputs(w, per_mode=True)
+        check_prefill(f"per_mode_{inp['io']}", inp, w.K, 0)
+
+
+def test_prefill_chunk_length_invariance():
+    """Every chunk length gives the oracle's result (chunking is exact, Eq. 6)."""
+    w = I.workload(1, B=1, L=257, K=3)
+    inp = I.make_prefill_inputs(w)
+    for Lc in (32, 64, 128):
+        check_prefill(f"Lc{Lc}", inp, 3, Lc)
+
+
+def test_prefill_resume_split():
+    """prefill(0:L1) -> state -> prefill(L1:L) matches the oracle over the whole sequence."""
+    import torch
+    essh = _essh()
+    w = I.workload(1, B=2, L=400, K=3)
+    inp = I.make_prefill_inputs(w)
+    L1 = 137
+    part = lambda lo, hi: {k: (inp[k][:, lo:hi] if k in ("v", "delta", "g_w", "g_r") else inp[k])
+                           for k in inp}
+    a, b = part(0, L1), part(L1, w.L)
+    log("resume: two prefill calls")
+    ya, sa = run_gpu_prefill(a, 3, 64)
+    db = device_inputs(b)
+    yb, sb = essh.prefill(db["v"], db["delta"], db["g_w"], db["g_r"], db["rho"], db["theta"], db["c"],
+                          K_T=3, Lc=64, state_in=sa)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.prefill(**oracle_inputs(inp), K_T=3)
+    y = np.concatenate([to_host_f64(ya), to_host_f64(yb)], axis=1)
+    assert block_err(y[:, :, :3], y_ref[:, :, :3], 2) <= TOL["bf16"]
+    assert block_err(to_host_f64(sb)[:, :3], s_ref[:, :3], 1) <= TOL["bf16"]
+
+
+def test_prefill_truncation_bit_identical_and_untouched():
+    """Tier K_T equals the first K_T channels of tier K bit for bit; discarded channels of y
+    and of the state keep their contents; NaN in discarded channels cannot leak."""
+    import torch
+    essh = _essh()
+    w = I.workload(1, B=2, L=200, K=8)
+    inp = I.make_prefill_inputs(w)
+    log("truncation: full tier")
+    y_full, s_full = run_gpu_prefill(inp, 8, 64)
+    poisoned = {k: np.array(v, copy=True) if isinstance(v, np.ndarray) else v for k, v in inp.items()}
+    for key in ("v", "g_w", "g_r"):
+        poisoned[key][:, :, 5:] = 0x7FC0          # bf16 NaN
+    poisoned["delta"][:, :, 5:] = np.nan
+    for key in ("rho", "theta", "c"):
+        poisoned[key][5:] = np.nan
+    for K_T in (1, 3, 5):
+        log(f"truncation: K_T={K_T}")
+        d = device_inputs(poisoned)
+        sentinel = torch.full_like(d["v"], 7.0)
+        s_sent = torch.full((2, 8, w.m, 2, w.P), 5.0, device="cuda")
+        dims = essh.make_dims(2, w.L, 8, w.m, w.P, K_T, 64, False, "bf16")
+        st = essh.essh_mixer_prefill(dims, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"],
+                                     d["c"], None, s_sent, sentinel)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert torch.equal(sentinel[:, :, :K_T], y_full[:, :, :K_T])
+        assert torch.all(sentinel[:, :, K_T:] == 7.0)
+        assert torch.equal(s_sent[:, :K_T], s_full[:, :K_T])
+        assert torch.all(s_sent[:, K_T:] == 5.0)
+        assert torch.isfinite(sentinel.float()).all()
+
+
+def test_prefill_empty_inputs():
+    """L = 0 passes the state through; B = 0 is a no-op."""
+    import torch
+    essh = _essh()
+    w = I.workload(1, B=2, L=0, K=3)
+    dims = essh.make_dims(2, 0, 3, w.m, w.P, 3, 64)
+    v = torch.empty((2, 0, 3, w.P), dtype=torch.bfloat16, device="cuda")
+    dl = torch.empty((2, 0, 3), device="cuda")
+    g = torch.empty((2, 0, 3), dtype=torch.bfloat16, device="cuda")
+    tab = torch.rand((3, w.m), device="cuda") * 0.5 + 0.4
+    c = torch.rand((3, w.m, 2), device="cuda")
+    s_in = torch.randn((2, 3, w.m, 2, w.P), device="cuda")
+    s_out = torch.zeros_like(s_in)
+    y = torch.empty((2, 1, 3, w.P), dtype=torch.bfloat16, device="cuda")  # unused, must be non-null
+    assert essh.essh_mixer_prefill(dims, v if v.numel() else y, dl if dl.numel() else tab, g if g.numel() else y,
+                                   g if g.numel() else y, tab, tab, c, s_in, s_out, y) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(s_out, s_in)
+    dims0 = essh.make_dims(0, 5, 3, w.m, w.P, 3, 64)
+    assert essh.essh_mixer_prefill(dims0, y, tab, y, y, tab, tab, c, None, None, y) == 0
+
+
+# ---------------------------------------------------------------------------
+# Full workload sizes: sampled channels against the oracle
+# ---------------------------------------------------------------------------
+
+FULL = [(1, 24, [(0, 0), (3, 11), (7, 23)]),
+        (2, 32, [(0, 0), (9, 17), (15, 31)]),
+        (4, 24, [(0, 0), (0, 13), (0, 23)])]
+
+
+@pytest.mark.parametrize("widx,K_T,samples", FULL, ids=["mixer370m_full", "mixer1p5b_full", "dna128k_full"])
+def test_prefill_full_size_sampled(widx, K_T, samples):
+    w = I.workload(widx)
+    inp = I.make_prefill_inputs(w)
+    log(f"full size workload {w.name}: GPU prefill K_T={K_T} Lc={w.Lc}")
+    y, st = run_gpu_prefill(inp, K_T, w.Lc)
+    tol = TOL[inp["io"]]
+    for b, k in samples:
+        sl = {key: (inp[key][b:b + 1, :, k:k + 1] if key in ("v", "delta", "g_w", "g_r") else
+                    inp[key][k:k + 1] if key in ("rho", "theta", "c") else inp[key]) for key in inp}
+        y_ref, s_ref = oracle.prefill(**oracle_inputs(sl))
+        yk = to_host_f64(y[b:b + 1, :, k:k + 1])
+        sk = to_host_f64(st[b:b + 1, k:k + 1])
+        ey, es = block_err(yk, y_ref, 2), block_err(sk, s_ref, 1)
+        log(f"  (b={b}, k={k}): y err {ey:.3e}, state err {es:.3e}")
+        assert ey <= tol and es <= tol
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+def _decode_case(NL, B, K, m, P, io, per_mode=False, seed=5):
+    rng = np.random.default_rng(seed)
+    w = I.Workload(99, "decode_case", B=B, L=1, K=K, m=m, P=P, Lc=64, io=io,
+                   rho_lo=0.95, rho_hi=0.9999, tiers=(K,))
+    params = [I.draw_params(rng, K, m, w.rho_lo, w.rho_hi) for _ in range(NL)]
+    rho = np.stack([p[0] for p in params]); theta = np.stack([p[1] for p in params])
+    c = np.stack([p[2] for p in params])
+    v, dl, gw, gr = I.draw_tokens(rng, NL, B, K, P, io, per_mode_m=m if per_mode else None)
+    state = rng.normal(0, 2.0, size=(NL, B, K, m, 2, P)).astype(np.float32)
+    return dict(v=v, delta=dl, g_w=gw, g_r=gr, rho=rho, theta=theta, c=c, io=io), state
+
+
+@pytest.mark.parametrize("io,per_mode,m,P", [("bf16", False, 8, 128), ("bf16", False, 4, 64),
+                                             ("f32", False, 4, 16), ("bf16", True, 2, 32),
+                                             ("f32", True, 1, 16)])
+def test_decode_step_matches_oracle(io, per_mode, m, P):
+    import torch
+    essh = _essh()
+    inp, state = _decode_case(3, 2, 6, m, P, io, per_mode)
+    for K_T in (2, 6):
+        log(f"decode io={io} per_mode={per_mode} m={m} P={P} K_T={K_T}")
+        d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
+        st = to_dev(state.copy())
+        y = torch.full_like(d["v"], 3.0)
+        essh.decode_step(st, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                         K_T=K_T, y=y)
+        torch.cuda.synchronize()
+        ox = {k: I.as_f64(inp[k], io) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
+        y_ref, s_ref = oracle.decode_step(state.astype(np.float64), **ox, K_T=K_T)
+        tol = TOL[io]
+        ey = block_err(to_host_f64(y)[:, :, :K_T].reshape(-1, K_T, P), y_ref[:, :, :K_T].reshape(-1, K_T, P), 1)
+        es = block_err(to_host_f64(st)[:, :, :K_T].reshape(-1, K_T, m * 2 * P),
+                       s_ref[:, :, :K_T].reshape(-1, K_T, m * 2 * P), 1)
+        log(f"  y err {ey:.3e}, state err {es:.3e}")
+        assert ey <= tol and es <= tol
+        assert torch.all(y[:, :, K_T:] == 3.0)
+        assert torch.equal(st[:, :, K_T:], to_dev(state[:, :, K_T:].copy()))
+
+
+def test_decode_iterated_equals_prefill():
+    """Decoding L tokens one by one from a zero state reproduces the prefill of those L tokens."""
+    import torch
+    essh = _essh()
+    w = I.workload(2, B=1, L=96, K=4)
+    inp = I.make_prefill_inputs(w)
+    d = device_inputs(inp)
+    log("decode-iterated vs prefill")
+    y_pf, s_pf = essh.prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], Lc=64)
+    st = torch.zeros((1, 1, 4, w.m, 2, w.P), device="cuda")
+    ys = []
+    for t in range(w.L):
+        y = essh.decode_step(st, d["v"][:, t][None].contiguous(), d["delta"][:, t][None].contiguous(),
+                             d["g_w"][:, t][None].contiguous(), d["g_r"][:, t][None].contiguous(),
+                             d["rho"][None], d["theta"][None], d["c"][None])
+        ys.append(y[0])
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    y_ref, s_ref = oracle.prefill(**oracle_inputs(inp))
+    assert block_err(to_host_f64(y_dec), y_ref, 2) <= TOL["bf16"]
+    assert block_err(to_host_f64(st[0]), s_ref, 1) <= 1e-5     # fp32 recurrence on both sides
+    assert block_err(to_host_f64(y_dec), to_host_f64(y_pf), 2) <= TOL["bf16"]
+    assert block_err(to_host_f64(s_pf), to_host_f64(st[0]), 1) <= 1e-3
+
+
+def test_decode_after_prefill_full_shape_sampled():
+    """The decode workload shape: 24 layers x (K=32, m=8, P=128), state pre-filled by a seeded
+    prefill, then steps; sampled (layer, channel) pairs are checked against the oracle."""
+    import torch
+    essh = _essh()
+    w = I.workload(3)
+    context, steps = 512, 8
+    dec = I.make_decode_inputs(w, n_steps=steps, context=context)
+    NL = w.layers
+    log(f"decode workload: {NL} layers, context {context}, {steps} steps")
+    state = torch.zeros((NL, 1, w.K, w.m, 2, w.P), device="cuda")
+    rho, theta, c = to_dev(dec["rho"]), to_dev(dec["theta"]), to_dev(dec["c"])
+    for l in range(NL):
+        _, st = essh.prefill(to_dev(dec["ctx_v"][l]), to_dev(dec["ctx_delta"][l]), to_dev(dec["ctx_g_w"][l]),
+                             to_dev(dec["ctx_g_r"][l]), rho[l], theta[l], c[l], Lc=64)
+        state[l] = st
+    ys = []
+    for s in range(steps):
+        ys.append(essh.decode_step(state, to_dev(dec["step_v"][s]), to_dev(dec["step_delta"][s]),
+                                   to_dev(dec["step_g_w"][s]), to_dev(dec["step_g_r"][s]), rho, theta, c).clone())
+    torch.cuda.synchronize()
+    for l, k in ((0, 0), (11, 17), (23, 31)):
+        seq = lambda a, b: np.concatenate([a[l][:, :, k:k + 1], np.moveaxis(b[:, l], 0, 1)[:, :, k:k + 1]], axis=1)
+        ox = dict(v=I.as_f64(seq(dec["ctx_v"], dec["step_v"]), "bf16"),
+                  delta=seq(dec["ctx_delta"], dec["step_delta"]).astype(np.float64),
+                  g_w=I.as_f64(seq(dec["ctx_g_w"], dec["step_g_w"]), "bf16"),
+                  g_r=I.as_f64(seq(dec["ctx_g_r"], dec["step_g_r"]), "bf16"),
+                  rho=dec["rho"][l][k:k + 1].astype(np.float64), theta=dec["theta"][l][k:k + 1].astype(np.float64),
+                  c=dec["c"][l][k:k + 1].astype(np.float64))
+        y_ref, s_ref = oracle.prefill(**ox)
+        y_dec = np.stack([to_host_f64(ys[s][l, :, k:k + 1]) for s in range(steps)], axis=1)
+        ey = block_err(y_dec, y_ref[:, context:], 2)
+        es = block_err(to_host_f64(state[l, :, k:k + 1]), s_ref, 1)
+        log(f"  layer {l} channel {k}: y err {ey:.3e}, state err {es:.3e}")
+        assert ey <= TOL["bf16"] and es <= TOL["bf16"]
