@@ -27,6 +27,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
+    # LDS tiles are addressed through vector types of several element types
+    "-fno-strict-aliasing",
     # packed fp32 (v_pk_*_f32) selection off
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

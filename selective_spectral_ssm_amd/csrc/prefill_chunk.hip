@@ -46,7 +46,8 @@ namespace essh {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float LOG2E = 1.4426950408889634f;
@@ -367,28 +368,38 @@ prefill_chunk_kernel(PrefillArgs a, int seg_chunks) {
                 vf[ks][nt] = *reinterpret_cast<const bf16x8_t*>(&Vw[(blk * WCOLS + pph) * 8]);
             }
         }
-        // state fragments as the A operand of the carry product (hi + lo)
-        i16x4_t shi[NTW], slo[NTW];
+        // State fragments as the A operand of the carry product.  The K axis
+        // of one 16x16x32 product holds (state row, hi/lo half) pairs: lane
+        // (g, col) supplies the bf16 hi parts of its state rows 4g..4g+3 in
+        // elements 0..3 and the lo parts in elements 4..7; the B operand
+        // repeats the matching carry-matrix entries in both halves.  Keeping
+        // every product of the accumulation chain on the same MFMA shape
+        // avoids a dependent 16x16x16 -> 16x16x32 accumulator hand-off.
+        bf16x8_t sf[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
+            u16x8_t raw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float x = st[nt][i];
                 const uint16_t hb = f32_to_bf16(x);
-                shi[nt][i] = (short)hb;
-                slo[nt][i] = (short)f32_to_bf16(x - bf16_to_f32(hb));
+                raw[i] = hb;
+                raw[4 + i] = f32_to_bf16(x - bf16_to_f32(hb));
             }
+            sf[nt] = __builtin_bit_cast(bf16x8_t, raw);
         }
 
         const int qu = C::QU;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
             const int tr = mt * 16 + col;          // position (row of G, A) owned by this lane
+            // carry term first: y^T += H^T A^T over the (state row, hi/lo) axis
+            const u16x4_t a4 = *reinterpret_cast<const u16x4_t*>(&sm.A[tr * 16 + ((g ^ ((tr >> 2) & 3)) * 4)]);
+            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, u16x8_t{a4[0], a4[1], a4[2], a4[3], a4[0], a4[1], a4[2], a4[3]});
             f32x4_t acc[NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            constexpr int dummy = 0;
-            (void)dummy;
+            for (int nt = 0; nt < NTW; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[nt], af, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             const int nks = mt / 2 + 1;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
@@ -399,12 +410,6 @@ prefill_chunk_kernel(PrefillArgs a, int seg_chunks) {
                     for (int nt = 0; nt < NTW; ++nt)
                         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks][nt], gf, acc[nt], 0, 0, 0);
                 }
-            }
-            const i16x4_t af = *reinterpret_cast<const i16x4_t*>(&sm.A[tr * 16 + ((g ^ ((tr >> 2) & 3)) * 4)]);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(shi[nt], af, acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(slo[nt], af, acc[nt], 0, 0, 0);
             }
             // lane holds y(t = tr, p = 16nt + 4g + i), i = 0..3
             const float grv = sm.gr[tr];
