@@ -109,8 +109,14 @@ essh_status essh_mixer_prefill(const essh_dims* d,
     a.y = y;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    hipError_t e = chunked ? launch_prefill_chunked(a, d->m, d->P, stream)
-                           : launch_prefill_sequential(a, d->m, d->P, d->io_dtype, stream);
+    hipError_t e;
+    if (chunked) {
+        ScanPlan plan = plan_chunked(d->B, d->L, d->K_T, d->m, d->P, lc);
+        bind_workspace(plan, workspace, d->m, d->P);
+        e = launch_prefill_chunked(a, d->m, d->P, plan, stream);
+    } else {
+        e = launch_prefill_sequential(a, d->m, d->P, d->io_dtype, stream);
+    }
     return from_hip(e);
 }
 

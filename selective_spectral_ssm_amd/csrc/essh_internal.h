@@ -70,11 +70,45 @@ struct DecodeArgs {
     void* y;
 };
 
+// Work split of the chunked prefill.  nseq = B * K_T sequences of nchunks
+// chunks; each sequence is cut into nseg segments of seg_chunks chunks, one
+// workgroup per (sequence, segment).  With nseg > 1 the workspace holds the
+// look-back state of the segmented scan:
+//   hdr   [SCAN_HDR_WORDS]          epoch, error bits and completion count (first 128-byte
+//                                   line), then 8 ticket and 8 done counters, one line each
+//   flags [nseq * nseg]             (epoch tag << 2) | FLAG_AGG / FLAG_INCL
+//   lam   [nseq * nseg][2m]         segment transfer Lambda_j (re, im)
+//   agg   [nseq * nseg][2m][P]      end state reached from a zero entering state
+//   incl  [nseq * nseg][2m][P]      true end state
+// The header must be zero before the first launch that uses the workspace;
+// each launch leaves it re-armed for the next one.
+enum {
+    SCAN_HDR_EPOCH = 0,
+    SCAN_HDR_ERROR = 1,
+    SCAN_HDR_XDONE = 2,
+    SCAN_HDR_STRIDE = 32,                    // one 128-byte line per counter
+    SCAN_HDR_TICKET0 = 1 * SCAN_HDR_STRIDE,
+    SCAN_HDR_DONE0 = 9 * SCAN_HDR_STRIDE,
+    SCAN_HDR_WORDS = 17 * SCAN_HDR_STRIDE
+};
+enum : unsigned { SCAN_ERR_TIMEOUT = 1u, SCAN_ERR_TICKET = 2u };
+
+struct ScanPlan {
+    int nseq, nchunks, seg_chunks, nseg, nblocks;
+    unsigned* hdr;
+    unsigned* flags;
+    float* lam;
+    float* agg;
+    float* incl;
+};
+
 // Launchers (host side).  Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_sequential(const PrefillArgs& a, int m, int P, int io_dtype, hipStream_t s);
-hipError_t launch_prefill_chunked(const PrefillArgs& a, int m, int P, hipStream_t s);
 bool chunked_supported(int m, int P, int Lc, int io_dtype, int per_mode);
+ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc);
 size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc);
+void bind_workspace(ScanPlan& plan, void* workspace, int m, int P);
+hipError_t launch_prefill_chunked(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int B, int K, int K_T, int m, int P, hipStream_t s);

@@ -158,7 +158,8 @@ class Prefill:
         self.state_out = (torch.zeros((B, K, m, 2, P), dtype=torch.float32, device=v.device)
                           if want_state else None)
         ws = essh_prefill_workspace_bytes(self.dims)
-        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=v.device) if ws else None
+        # zero-filled once: the library keeps the look-back header armed across calls
+        self.workspace = torch.zeros(max(ws, 1), dtype=torch.uint8, device=v.device) if ws else None
         self.ws_bytes = ws
         self.stream = stream
 

@@ -104,3 +104,23 @@ def test_workspace_query_is_total(lib):
         assert essh.essh_prefill_workspace_bytes(d) >= 0
     d = essh.make_dims(8, 2048, 24, 3, 64, 24, 64)   # unsupported m -> 0
     assert essh.essh_prefill_workspace_bytes(d) == 0
+
+
+def _call_ws(dims, ws, ws_bytes):
+    p = [ctypes.c_void_p(FAKE)] * 7
+    lib = essh.lib()
+    return lib.essh_mixer_prefill(ctypes.byref(dims), *p, None, None, ctypes.c_void_p(FAKE),
+                                  None if ws is None else ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_segmented_prefill_needs_a_workspace(lib):
+    """Few (batch row, channel) sequences -> the scan is segmented and needs look-back space:
+    at least the aggregate and inclusive states (2 x 2m x P fp32) of every segment."""
+    d = essh.make_dims(1, 131072, 24, 4, 64, 6, 128)
+    need = essh.essh_prefill_workspace_bytes(d)
+    nchunks = 131072 // 128
+    assert need >= 2 * (1 * 6) * 2 * 2 * 4 * 64 * 4          # at least two segments per sequence
+    assert need <= 2 * (1 * 6) * nchunks * 2 * 4 * 64 * 4 + 2 * 6 * nchunks * 64 + 4096
+    assert _call_ws(d, None, 0) == essh.ESSH_ERR_WORKSPACE
+    assert _call_ws(d, FAKE * 16, need - 1) == essh.ESSH_ERR_WORKSPACE
+    assert _call_ws(d, FAKE * 16 + 16, need) == essh.ESSH_ERR_WORKSPACE     # not 256-byte aligned

@@ -128,6 +128,47 @@ def test_prefill_resume_split():
     assert block_err(to_host_f64(sb)[:, :3], s_ref[:, :3], 1) <= TOL["bf16"]
 
 
+def test_prefill_workspace_reuse_and_state_alias():
+    """One workspace serves consecutive calls (the look-back header re-arms itself), results are
+    identical call after call, and state_in may alias state_out across segments."""
+    import torch
+    essh = _essh()
+    w = I.workload(1, B=1, L=1100, K=3)             # 3 sequences of 18 chunks: segmented scan
+    inp = I.make_prefill_inputs(w)
+    d = device_inputs(inp)
+    rng = np.random.default_rng(7)
+    s0 = rng.normal(0, 2.0, size=(1, 3, w.m, 2, w.P)).astype(np.float32)
+    call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], K_T=3, Lc=64,
+                        state_in=to_dev(s0))
+    assert call.ws_bytes > 0, "expected the segmented scan for this shape"
+    log("workspace reuse: three calls on one workspace")
+    ys = []
+    for _ in range(3):
+        y, st = call.run()
+        torch.cuda.synchronize()
+        ys.append((y.clone(), st.clone()))
+        hdr = call.workspace[:17 * 128].view(torch.int32).cpu().numpy()
+        # line 0: epoch, error bits, completion count; lines 1-8 tickets, 9-16 done counters
+        counters = hdr[32::32]
+        assert hdr[1] == 0 and hdr[2] == 0 and not counters.any(), f"look-back header not re-armed: {hdr[::32]}"
+    assert hdr[0] == 3
+    for y, st in ys[1:]:
+        assert torch.equal(y, ys[0][0]) and torch.equal(st, ys[0][1])
+    y_ref, s_ref = oracle.prefill(**oracle_inputs(inp), K_T=3, state_in=s0)
+    assert block_err(to_host_f64(ys[0][0]), y_ref, 2) <= TOL["bf16"]
+    assert block_err(to_host_f64(ys[0][1]), s_ref, 1) <= TOL["bf16"]
+    # state_in aliasing state_out: the entering state is read before any segment writes
+    log("workspace reuse: aliased state")
+    state = to_dev(s0.copy())
+    y2 = torch.empty_like(d["v"])
+    ws = torch.zeros(call.ws_bytes, dtype=torch.uint8, device="cuda")
+    rc = essh.essh_mixer_prefill(call.dims, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                                 state, state, y2, ws, call.ws_bytes)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y2, ys[0][0]) and torch.equal(state, ys[0][1])
+
+
 def test_prefill_truncation_bit_identical_and_untouched():
     """Tier K_T equals the first K_T channels of tier K bit for bit; discarded channels of y
     and of the state keep their contents; NaN in discarded channels cannot leak."""
@@ -149,8 +190,10 @@ def test_prefill_truncation_bit_identical_and_untouched():
         sentinel = torch.full_like(d["v"], 7.0)
         s_sent = torch.full((2, 8, w.m, 2, w.P), 5.0, device="cuda")
         dims = essh.make_dims(2, w.L, 8, w.m, w.P, K_T, 64, False, "bf16")
+        nws = essh.essh_prefill_workspace_bytes(dims)
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device="cuda")
         st = essh.essh_mixer_prefill(dims, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"],
-                                     d["c"], None, s_sent, sentinel)
+                                     d["c"], None, s_sent, sentinel, ws, nws)
         assert st == 0
         torch.cuda.synchronize()
         assert torch.equal(sentinel[:, :, :K_T], y_full[:, :, :K_T])
