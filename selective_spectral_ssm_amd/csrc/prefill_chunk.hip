@@ -1,54 +1,58 @@
 // prefill_chunk.hip -- chunked parallel scan of the ESSH selective mixer on MFMA.
 //
 // ESSH paper, Sec. 4.3 "Chunked parallel training" and Fig. 2A: positions are
-// split into chunks of Lc; inside a chunk the source-to-target contributions
-// are a dense causal matrix G_k applied by matrix multiplication, and only the
-// 2 m P mode-state entries of a channel cross a chunk boundary.  Eq. 6 (the
-// transition product rho^{t-s} e^{-sum delta} R(theta (t-s))) makes this
-// exact.  For a chunk [t0, t0+n) and chunk-local inclusive clock sums
-// qh(r) = sum_{l<=r} delta(t0+l), with lambda_j = rho_j e^{i theta_j}:
+// split into chunks; inside a chunk the source-to-target contributions form a
+// dense causal matrix applied by matrix multiplication, and only the 2 m P
+// mode-state entries of a channel cross a chunk boundary.  Eq. 6 (the
+// transition product rho^{t-s} e^{-sum delta} R(theta (t-s))) makes this exact.
 //
-//   y(r)   = g_r(r) [ sum_{s<=r} e^{-(qh(r)-qh(s))} g_w(s) psi(r-s) v(s)        (intra, G V)
-//                   + e^{-qh(r)} sum_j Re(c_j lambda_j^{r+1} h_j) ]             (carry,  A H)
-//   h_j'   = lambda_j^n e^{-qh(n-1)} h_j
-//            + sum_s lambda_j^{n-1-s} e^{-(qh(n-1)-qh(s))} g_w(s) v(s)          (end state, W V)
+// Sub-blocks.  A chunk of Lc positions is processed as 16-position sub-blocks
+// [T0, T0+16) carrying the mode state h (complex, per mode j and value p)
+// from one to the next.  With lambda_j = rho_j e^{i theta_j}, psi(tau) =
+// sum_j Re(c_j lambda_j^tau) and the clock measured from the sub-block start,
+//   a(t) = e^{-(qh(t) - qh(T0-1))},   b(s) = e^{qh(s) - qh(T0-1)} g_w(s),
+// the recurrence over the sub-block gives, for t, s in [T0, T0+16):
+//   y(t) = g_r(t) a(t) [ sum_{s<=t} psi(t-s) b(s) v(s)
+//                        + sum_j Re(c_j lambda_j^{t-T0+1} h_j) ]          (intra + carry)
+//   h_j' = A_T ( lambda_j^16 h_j + sum_s lambda_j^{T0+15-s} b(s) v(s) ),
+//   A_T = e^{-(qh(T0+15) - qh(T0-1))}.
+// The matrices psi(t-s) [s<=t], Re/Im(c_j lambda_j^{t-T0+1}) and
+// Re/Im(lambda_j^{15-s+T0}) are the same for every sub-block, so they are
+// built once per channel as MFMA operands held in registers; per sub-block
+// only v is scaled by b(s) and y by g_r(t) a(t).  Per 16 value columns that
+// is three v_mfma_f32_16x16x32_bf16:
+//   y^T = [b.v ; H_hi]^T [Psi^T ; C^T]         K = 16 positions + 16 state rows
+//   M   = [Lpow_hi Lpow_lo] [b.v ; b.v]        K = 16 positions x hi/lo, once for
+//                                              the bf16 hi and once for the lo part of b.v
+// and h' = A_T (lambda^16 h + M) on the VALU.  b(s) grows within a sub-block;
+// a sub-block whose clock span could overflow it, and a ragged last one, take
+// an exact per-element path instead (same MFMA shapes, operands from exps).
 //
-// with psi(tau) = sum_j Re(c_j lambda_j^tau).  Channels are independent
-// (Sec. 4.1), so a workgroup owns one (batch row, channel) and walks the
-// chunks of a segment of positions in order, keeping the channel's mode state
-// in registers.
+// Channels are independent (Sec. 4.1), so a workgroup owns one (batch row,
+// channel) and walks the chunks of a segment of positions in order, keeping
+// the channel's mode state in registers.
 //
 // Segmented scan.  When batch rows x retained channels alone cannot fill the
 // GPU, each sequence of chunks is cut into segments handled by different
 // workgroups.  The state entering a segment is the composition of the affine
-// chunk maps h -> Lambda h + S before it (the same Eq. 6 algebra one level
-// up).  A workgroup (i) sweeps its segment once computing only the end state
-// reached from a zero state (its aggregate S_seg and transfer Lambda_seg),
-// (ii) publishes it, (iii) obtains its entering state by a decoupled
-// look-back over its predecessors' published aggregates / inclusive states,
-// publishes its own inclusive state, and (iv) sweeps the segment again with
-// the true entering state, now producing y.  The second sweep re-reads v,
-// which the first sweep has just brought into the caches.
+// maps h -> Lambda h + S of the chunks before it (the same Eq. 6 algebra one
+// level up).  A workgroup (i) sweeps its segment once computing only the end
+// state reached from a zero state (its aggregate S_seg and transfer
+// Lambda_seg), (ii) publishes it, (iii) obtains its entering state by a
+// decoupled look-back over its predecessors' published aggregates / inclusive
+// states, publishes its own inclusive state, and (iv) sweeps the segment
+// again with the true entering state, now producing y.  The second sweep
+// re-reads v, which the first sweep has just brought into the caches.
 //
 // gfx950 mapping
 //   * Each wave owns 16*NTW value columns for all positions: its share of the
 //     state lives in VGPRs in the 16x16 MFMA accumulator layout (lane (g,col)
 //     holds state rows 4g..4g+3 = (mode 2g, re/im), (mode 2g+1, re/im) of
-//     column col).
-//   * All three products use v_mfma_f32_16x16x32_bf16.  The intra-chunk
-//     product is computed transposed, Y^T = V^T G^T, so that the V fragment
-//     a lane holds (8 consecutive positions of one value column) is the A
-//     operand of Y^T and the B operand of the end-state product W V.  The
-//     carry product packs (state row, hi/lo half) into its K axis.  Every
-//     product of one accumulation chain has the same MFMA shape.
-//   * G and the carry matrix A are rounded once to bf16 (the output is bf16);
-//     W, which feeds the fp32 state, is split into bf16 hi + lo, and so is
-//     the state in the carry product, so the state path keeps ~16 bits.
-//   * v is streamed with 16-byte loads one chunk ahead of the arithmetic and
-//     written to LDS transposed ([t/8][column][8]) with a bank swizzle; y is
-//     staged through the same LDS region and written with 16-byte stores.
-//   * Clocks, gates and pole tables are staged in LDS; G, W, A are built
-//     cooperatively once per chunk and read by every wave.
+//     column col).  Every product of one accumulation chain has one MFMA shape.
+//   * v tiles are loaded with 16-byte loads one chunk ahead and stored to LDS
+//     row-major with an XOR swizzle of 16-byte units; the MFMA fragments (four
+//     consecutive positions of one column) come back with ds_read_b64_tr_b16.
+//     y is staged in place and written with 16-byte stores.
 //   * Look-back messages are written and read with agent-scope atomic
 //     accesses (they bypass the per-XCD L2), flags carry a per-launch epoch,
 //     and every wait is bounded.
@@ -61,14 +65,19 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr float LOG2E = 1.4426950408889634f;
+// Largest clock span of a sub-block, in log2 units, that the factored path
+// takes: b(s) <= 2^64 g_w(s) keeps b(s) v(s) far from overflow.
+constexpr float SPAN2_FAST_MAX = 64.f;
 
 // Look-back flag kinds (low two bits of a flag word; the rest is the epoch tag).
 constexpr unsigned FLAG_AGG = 1u;    // aggregate (end state from a zero entering state) and transfer
 constexpr unsigned FLAG_INCL = 2u;   // inclusive state (true state after the segment)
-// Upper bound on polls of one flag (each poll is a memory round trip plus a
-// short sleep, so this is tens of milliseconds); exceeding it records
+// Upper bound on polls of one flag window (each poll is a memory round trip
+// plus a short sleep, so this is tens of milliseconds); exceeding it records
 // SCAN_ERR_TIMEOUT in the workspace header instead of waiting forever.
 constexpr int SPIN_LIMIT = 1 << 16;
 
@@ -80,39 +89,44 @@ struct Cfg {
     static constexpr int NTW = NT / NW;             // value tiles per wave
     static constexpr int THREADS = 64 * NW;
     static constexpr int WCOLS = 16 * NTW;          // value columns per wave
-    static constexpr int MT = LC / 16;              // 16-position tiles
-    static constexpr int KS = LC / 32;              // 32-deep k steps
-    static constexpr int UNITS = LC / 8;            // 16-byte units per G/W row
-    static constexpr int GSWZ = (UNITS < 8 ? UNITS : 8) - 1;
+    static constexpr int NSB = LC / 16;             // 16-position sub-blocks per chunk
     static constexpr int LPR = WCOLS / 8;           // lanes per v row (16 B each)
     static constexpr int RPI = 64 / LPR;            // v rows per wave load
     static constexpr int NLD = LC / RPI;            // wave loads per chunk
-    static constexpr int QU = WCOLS / 4;            // 8-byte units per staged y row
-    static constexpr int YROWS128 = 64 / WCOLS;     // staged y rows per 128 bytes
     static constexpr int CPL = (LC + 63) / 64;     // control positions per lane of wave 0
+    // v tile rows are P bf16 = P/8 16-byte units; unit u of row r is stored at
+    // unit u ^ swz(r), swz(r) = 2 * ((r / RP256) % (P/16)), which spreads the
+    // 16 rows a transposing fragment read touches over all LDS banks.
+    static constexpr int RP256 = P >= 128 ? 1 : 128 / P;   // rows per 256 bytes
+    static constexpr int SWZ_MASK = P / 16 - 1;
     static_assert(P % 16 == 0 && NT % NW == 0, "P must be 16, 32, 64 or 128");
     static_assert(LC % 32 == 0 && LC <= 128, "chunk length must be 32, 64 or 128");
     static_assert(M >= 1 && M <= 8, "1..8 modes");
     static_assert(LC % RPI == 0, "v tile loads must tile the chunk");
 };
 
+// Per-chunk staged data.
 template <class C>
-struct __align__(16) Smem {
+struct __align__(16) Stage {
     float q2[C::LC];                 // chunk-local inclusive clock sum * log2(e)
-    float eq[C::LC];                 // exp(-chunk-local inclusive clock sum)
     float gw[C::LC];                 // write gate
     float gr[C::LC];                 // read gate
-    float psi[C::LC];                // sum_j Re(c_j lambda_j^tau)
-    float2 pw[C::LC + 1][C::M];      // lambda_j^tau
-    float2 cpw[C::LC + 1][C::M];     // c_j lambda_j^tau
-    alignas(16) uint16_t G[C::LC * C::LC];        // bf16, row t, swizzled 16-byte units over s
-    alignas(16) uint16_t Whi[16 * C::LC];         // bf16, row (j,re/im), swizzled units over s
-    alignas(16) uint16_t Wlo[16 * C::LC];
-    alignas(16) uint16_t A[C::LC * 16];           // bf16, row t, 8-byte units over (j,re/im)
-    alignas(16) uint16_t V[C::NW][C::LC * C::WCOLS];   // per wave: v^T tile, then y staging
+    float bq[C::LC];                 // b(s) = e^{qh(s)-qh(T0-1)} g_w(s)   (0 beyond the chunk)
+    float ag[C::LC];                 // a(t) g_r(t) = e^{-(qh(t)-qh(T0-1))} g_r(t)
+    float2 blk[C::NSB];              // per sub-block: (A_T, 1 if the exact path is needed)
+    alignas(16) uint16_t V[C::LC * C::P];   // v tile [t][P] (swizzled units); y staged in place
+};
+
+template <class C>
+struct __align__(16) Smem {
+    Stage<C> stg;
+    float2 pw[17][C::M];             // lambda_j^tau, tau = 0..16
+    float2 cpw[17][C::M];            // c_j lambda_j^tau
+    float psi[16];                   // sum_j Re(c_j lambda_j^tau), tau = 0..15
     int ticket;
     unsigned epoch;
-    unsigned flag;
+    int lb_cnt;
+    int lb_found;
 };
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
@@ -147,6 +161,11 @@ __device__ __forceinline__ unsigned ld_agent_u(const unsigned* p) {
 }
 __device__ __forceinline__ void st_agent_u(unsigned* p, unsigned x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bf16x8_t to_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+__device__ __forceinline__ u16x8_t cat8(u16x4_t a, u16x4_t b) {
+    return u16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 template <class C, bool SEG>
@@ -208,28 +227,76 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const uint16_t* grg = static_cast<const uint16_t*>(a.g_r);
     uint16_t* yg = static_cast<uint16_t*>(a.y);
 
-    // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..LC ----------
-    for (int idx = tid; idx < (LC + 1) * M; idx += C::THREADS) {
+    // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16 ------------------------
+    for (int idx = tid; idx < 17 * M; idx += C::THREADS) {
         const int tau = idx / M, j = idx - tau * M;
         const float r = a.rho[k * M + j];
         const float th = a.theta[k * M + j];
         const float mag = tau == 0 ? 1.f : exp2f((float)tau * log2f(r));
-        // theta*tau reaches ~400 rad: form and reduce the angle in fp64.
-        double ang = (double)th * (double)tau;
-        ang -= 6.283185307179586476925 * rint(ang * 0.15915494309189533577);
         float sn, cs;
-        sincosf((float)ang, &sn, &cs);
+        sincosf(th * (float)tau, &sn, &cs);   // |theta tau| <= 16 pi
         const float pr = mag * cs, pi = mag * sn;
         sm.pw[tau][j] = make_float2(pr, pi);
         const float cr = a.c[(k * M + j) * 2], ci = a.c[(k * M + j) * 2 + 1];
         sm.cpw[tau][j] = make_float2(cr * pr - ci * pi, cr * pi + ci * pr);
     }
     __syncthreads();
-    for (int tau = tid; tau < LC; tau += C::THREADS) {
+    for (int tau = tid; tau < 16; tau += C::THREADS) {
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < M; ++j) s += sm.cpw[tau][j].x;
         sm.psi[tau] = s;
+    }
+    __syncthreads();
+
+    // ---- per-lane constant MFMA operands ------------------------------------------------
+    // by: B operand of the output product.  Lane (g, col) holds, for t = T0+col,
+    //   slots 0..3: psi(t-s) [s <= t] for s = T0+4g+e, and
+    //   slots 4..7: {Re, -Im}(c_j lambda_j^{t-T0+1}) for state rows 4g..4g+3.
+    // al: A operand of the state product.  Lane (g, col) holds, for state row
+    //   col = (j, re/im), {Re, Im}(lambda_j^{15-4g-e}) split into bf16 hi (slots
+    //   0..3) and lo (slots 4..7).
+    // l16: lambda_j^16 for this lane's modes 2g, 2g+1.
+    bf16x8_t by, al;
+    float l16[4];
+    {
+        u16x8_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 4 * g + e;
+            h[e] = f32_to_bf16(s <= col ? sm.psi[col - s] : 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * g + i, j = row >> 1;
+            float val = 0.f;
+            if (j < M) {
+                const float2 cp = sm.cpw[col + 1][j < M ? j : 0];
+                val = (row & 1) ? -cp.y : cp.x;
+            }
+            h[4 + i] = f32_to_bf16(val);
+        }
+        by = to_bf16x8(h);
+        const int jr = col >> 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float val = 0.f;
+            if (jr < M) {
+                const float2 pw = sm.pw[15 - 4 * g - e][jr < M ? jr : 0];
+                val = (col & 1) ? pw.y : pw.x;
+            }
+            const uint16_t hb = f32_to_bf16(val);
+            h[e] = hb;
+            h[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
+        }
+        al = to_bf16x8(h);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int j = 2 * g + hh;
+            const float2 p16 = j < M ? sm.pw[16][j < M ? j : 0] : make_float2(0.f, 0.f);
+            l16[2 * hh] = p16.x;
+            l16[2 * hh + 1] = p16.y;
+        }
     }
 
     // ---- state in the accumulator layout ---------------------------------------------
@@ -252,21 +319,26 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const int vrow_l = lane / C::LPR;          // row of this lane inside a wave load
     const int vunit = lane % C::LPR;           // 16-byte unit of this lane inside a row
     const size_t vcol0 = (size_t)wave * WCOLS + vunit * 8;
-    uint16_t* Vw = sm.V[wave];
+    Stage<C>& sg = sm.stg;
+    // element offset of (row r, first column of 16-byte unit u) in the v tile
+    auto vt_off = [&](int r, int u) { return r * P + ((u ^ (((r / C::RP256) & C::SWZ_MASK) << 1)) << 3); };
 
-    uint4 vreg[C::NLD];
-    float cd[C::CPL], cw[C::CPL], cr_[C::CPL];   // controls of the loaded chunk (wave 0 only)
+    // Loads of one chunk held in registers until they are staged into LDS.
+    struct ChunkRegs {
+        uint4 v[C::NLD];
+        float cd[C::CPL], cw[C::CPL], cr[C::CPL];   // controls (wave 0 only)
+    };
 
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](ChunkRegs& rg, int c) {
         const int t0 = c * LC;
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int t = t0 + i * C::RPI + vrow_l;
             if (t < L) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
-                vreg[i] = *reinterpret_cast<const uint4*>(vg + off);
+                rg.v[i] = *reinterpret_cast<const uint4*>(vg + off);
             } else {
-                vreg[i] = make_uint4(0, 0, 0, 0);
+                rg.v[i] = make_uint4(0, 0, 0, 0);
             }
         }
         if (wave == 0) {
@@ -276,46 +348,36 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int t = t0 + r;
                 if (r < LC && t < L) {
                     const size_t row = ((size_t)b * L + t) * K + k;
-                    cd[u] = a.delta[row];
-                    cw[u] = bf16_to_f32(gwg[row]);
-                    cr_[u] = bf16_to_f32(grg[row]);
+                    rg.cd[u] = a.delta[row];
+                    rg.cw[u] = bf16_to_f32(gwg[row]);
+                    rg.cr[u] = bf16_to_f32(grg[row]);
                 } else {
-                    cd[u] = 0.f;
-                    cw[u] = 0.f;
-                    cr_[u] = 0.f;
+                    rg.cd[u] = 0.f;
+                    rg.cw[u] = 0.f;
+                    rg.cr[u] = 0.f;
                 }
             }
         }
     };
 
-    // v tile and controls of the loaded chunk -> LDS, the chunk-local clock sums
-    // (wave 0 scans the controls it holds), then the loads of chunk `next`
-    // (if >= 0) are issued so that they overlap this chunk's arithmetic.
-    // v element (t, p') goes to ((t/8)*WCOLS + p'')*8 + t%8, where p'' permutes the
-    // low 3 bits of p' by a key of (t/8, p'/8) so a wave's 2-byte stores spread over
-    // all banks.  Ends with the shared tiles complete (barrier).
-    auto stage_chunk = [&](int next) {
-        __syncthreads();   // previous readers of the shared tiles are done
+    // v tile and controls of the loaded chunk (n valid positions) -> LDS, then the
+    // loads of chunk `next` (if >= 0) are issued so that they overlap this chunk's
+    // arithmetic.  Wave 0 scans the clock it holds and derives the per-position
+    // factors b(s), a(t) g_r(t) and the per-sub-block A_T.  Starts and ends with
+    // a barrier.
+    auto stage_chunk = [&](ChunkRegs& rg, int n, int next) {
+        __syncthreads();   // previous readers of the staged chunk are done
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
-            const int blk = tr >> 3, tt = tr & 7;
-            const uint32_t w4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int pp = vunit * 8 + e;
-                const int key = (blk * (WCOLS / 8) + (pp >> 3)) & 7;
-                const int pph = (pp & ~7) | ((pp & 7) ^ key);
-                const uint16_t val = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
-                Vw[(blk * WCOLS + pph) * 8 + tt] = val;
-            }
+            *reinterpret_cast<uint4*>(&sg.V[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
         }
         if (wave == 0) {
             float loc[C::CPL];
             float run = 0.f;
 #pragma unroll
             for (int u = 0; u < C::CPL; ++u) {
-                run += cd[u];
+                run += rg.cd[u];
                 loc[u] = run;
             }
             float incl = run;
@@ -329,213 +391,203 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int u = 0; u < C::CPL; ++u) {
                 const int idx = lane * C::CPL + u;
                 if (idx < LC) {
-                    const float q = excl + loc[u];
-                    sm.q2[idx] = q * LOG2E;
-                    sm.eq[idx] = expf(-q);
-                    sm.gw[idx] = cw[u];
-                    sm.gr[idx] = cr_[u];
+                    sg.q2[idx] = (excl + loc[u]) * LOG2E;
+                    sg.gw[idx] = rg.cw[u];
+                    sg.gr[idx] = rg.cr[u];
+                }
+            }
+            // same wave: its own LDS writes above are visible to these reads
+#pragma unroll
+            for (int u = 0; u < C::CPL; ++u) {
+                const int idx = lane * C::CPL + u;
+                if (idx < LC) {
+                    const int T0 = idx & ~15;
+                    const float qp = T0 > 0 ? sg.q2[T0 - 1] : 0.f;
+                    const float q = sg.q2[idx];
+                    sg.bq[idx] = idx < n ? exp2f(q - qp) * rg.cw[u] : 0.f;
+                    sg.ag[idx] = exp2f(qp - q) * rg.cr[u];
+                    const int T1 = min(T0 + 15, n - 1);
+                    if (idx == T1) {
+                        const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
+                        sg.blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
+                    }
                 }
             }
         }
-        if (next >= 0) load_chunk(next);
+        if (next >= 0) load_chunk(rg, next);
         __syncthreads();
     };
 
-    // W[(j,re/im)][s] = {Re,Im}(lambda_j^{n-1-s}) e^{-(qh(n-1)-qh(s))} g_w(s), hi + lo bf16.
-    auto build_W = [&](int n) {
-        const float qe = sm.q2[n - 1];
-        for (int idx = tid; idx < 16 * C::UNITS; idx += C::THREADS) {
-            const int row = idx / C::UNITS, u = idx - row * C::UNITS;
-            const int j = row >> 1, cmp = row & 1;
-            uint16_t hh[8], hl[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = u * 8 + e;
-                float val = 0.f;
-                if (j < M && s < n) {
-                    const float2 pw = sm.pw[n - 1 - s][j < M ? j : 0];
-                    val = (cmp ? pw.y : pw.x) * exp2f(sm.q2[s] - qe) * sm.gw[s];
-                }
-                const uint16_t hb = f32_to_bf16(val);
-                hh[e] = hb;
-                hl[e] = f32_to_bf16(val - bf16_to_f32(hb));
-            }
-            const int off = row * LC + ((u ^ (row & C::GSWZ)) * 8);
-            *reinterpret_cast<uint4*>(&sm.Whi[off]) =
-                make_uint4(pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7]));
-            *reinterpret_cast<uint4*>(&sm.Wlo[off]) =
-                make_uint4(pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7]));
-        }
+    // v fragment of sub-block T for tile nt: positions T0+4g..T0+4g+3 of column
+    // p = wave*WCOLS + nt*16 + col, by one transposing LDS read.  Within a group
+    // of 16 lanes, ds_read_b64_tr_b16 returns to lane i, element e, the (i%4)-th
+    // 16-bit value at the address of lane 4e + i/4; so lane (g, col) supplies
+    // the address of row T0 + 4g + col/4, columns 4*(col%4) .. +3 of the tile.
+    auto load_vfrag = [&](int T, int nt) -> u16x4_t {
+        const int r = T * 16 + 4 * g + (col >> 2);
+        const int p0 = wave * WCOLS + nt * 16 + 4 * (col & 3);
+        const int off = vt_off(r, p0 >> 3) + (p0 & 7);
+        const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sg.V[off]));
+        return __builtin_bit_cast(u16x4_t, x);
     };
 
-    // G[t][s] = e^{-(qh(t)-qh(s))} g_w(s) psi(t-s) for s <= t, bf16.  Only the
-    // 32-wide k blocks the MFMA loop reads are built.
-    auto build_G = [&]() {
-        for (int idx = tid; idx < LC * C::UNITS; idx += C::THREADS) {
-            const int r = idx / C::UNITS, u = idx - r * C::UNITS;
-            const int nks = ((r & ~15) + 15) / 32 + 1;
-            if (u >= 4 * nks) continue;
-            const float qr = sm.q2[r];
-            uint16_t h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = u * 8 + e;
-                float val = 0.f;
-                if (s <= r) val = exp2f(sm.q2[s] - qr) * sm.gw[s] * sm.psi[r - s];
-                h[e] = f32_to_bf16(val);
-            }
-            uint4 pk = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-            *reinterpret_cast<uint4*>(&sm.G[r * LC + ((u ^ (r & C::GSWZ)) * 8)]) = pk;
-        }
+    // y tile of sub-block T (lane holds y(t = T0+col, p0 + i), i < 4) -> staged in
+    // the v tile in place: each wave overwrites only its own columns of rows it
+    // has already read.
+    auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) {
+        const int t = T * 16 + col;
+        const int p0 = wave * WCOLS + nt * 16 + 4 * g;
+        const uint16_t h0 = f32_to_bf16(acc[0] * scale);
+        const uint16_t h1 = f32_to_bf16(acc[1] * scale);
+        const uint16_t h2 = f32_to_bf16(acc[2] * scale);
+        const uint16_t h3 = f32_to_bf16(acc[3] * scale);
+        *reinterpret_cast<uint2*>(&sg.V[vt_off(t, p0 >> 3) + (p0 & 7)]) = make_uint2(pack2(h0, h1), pack2(h2, h3));
     };
 
-    // A[t][(j,re/im)] = e^{-qh(t)} {Re, -Im}(c_j lambda_j^{t+1}), bf16, 8-byte units swizzled by t.
-    auto build_A = [&]() {
-        for (int idx = tid; idx < LC * 4; idx += C::THREADS) {
-            const int r = idx >> 2, q = idx & 3;
-            const float e = sm.eq[r];
-            uint16_t h[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kk = 4 * q + i, j = kk >> 1, cmp = kk & 1;
-                float val = 0.f;
-                if (j < M) {
-                    const float2 cp = sm.cpw[r + 1][j < M ? j : 0];
-                    val = e * (cmp ? -cp.y : cp.x);
-                }
-                h[i] = f32_to_bf16(val);
-            }
-            *reinterpret_cast<uint2*>(&sm.A[r * 16 + ((q ^ ((r >> 2) & 3)) * 4)]) =
-                make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-        }
+    auto hi4 = [&](const f32x4_t& x) -> u16x4_t {
+        return u16x4_t{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
     };
 
-    // v fragments: lane (g, col) holds v(s = 32ks + 8g .. +7, p = 16nt + col)
-    auto load_vf = [&](bf16x8_t (&vf)[C::KS][NTW]) {
+    // One sub-block: optional outputs, then the state update; tr accumulates the
+    // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
+    auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4]) {
+        const int T0 = T * 16;
+        const float2 bk = sg.blk[T];
+        u16x4_t vfr[NTW];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int nt = 0; nt < NTW; ++nt) vfr[nt] = load_vfrag(T, nt);
+        float lam[4];   // Lambda_T for modes 2g, 2g+1
+        if (bk.y == 0.f) {
+            // factored path: scale v by b(s), constant operands
+            const float4 b4 = *reinterpret_cast<const float4*>(&sg.bq[T0 + 4 * g]);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+            // b(s) v(s) split into bf16 hi + lo: the output product uses hi, the
+            // state product both, so the state keeps ~16 mantissa bits.
+            u16x4_t bv[NTW], bl[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const int blk = 4 * ks + g;
-                const int pp = nt * 16 + col;
-                const int key = (blk * (WCOLS / 8) + (pp >> 3)) & 7;
-                const int pph = (pp & ~7) | ((pp & 7) ^ key);
-                vf[ks][nt] = *reinterpret_cast<const bf16x8_t*>(&Vw[(blk * WCOLS + pph) * 8]);
-            }
-        }
-    };
-
-    // h <- Lambda h + W_hi V + W_lo V, with Lambda_j = lambda_j^n e^{-qh(n-1)}.
-    // Also folds Lambda into the running segment transfer (tr: modes 2g, 2g+1).
-    auto state_update = [&](f32x4_t (&st)[NTW], const bf16x8_t (&vf)[C::KS][NTW], int n, float (&tr)[4]) {
-        float lam[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = 2 * g + h;
-            float lr = 0.f, li = 0.f;
-            if (j < M) {
-                const float2 pw = sm.pw[n][j < M ? j : 0];
-                const float e = sm.eq[n - 1];
-                lr = pw.x * e;
-                li = pw.y * e;
-            }
-            lam[2 * h] = lr;
-            lam[2 * h + 1] = li;
-            const float ar = tr[2 * h], ai = tr[2 * h + 1];
-            tr[2 * h] = ar * lr - ai * li;
-            tr[2 * h + 1] = ar * li + ai * lr;
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            f32x4_t d;
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const float lr = lam[i], li = lam[i + 1];
-                const float hr = st[nt][i], hi = st[nt][i + 1];
-                d[i] = lr * hr - li * hi;
-                d[i + 1] = li * hr + lr * hi;
-            }
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const int off = col * LC + (((4 * ks + g) ^ (col & C::GSWZ)) * 8);
-                const bf16x8_t wh = *reinterpret_cast<const bf16x8_t*>(&sm.Whi[off]);
-                const bf16x8_t wl = *reinterpret_cast<const bf16x8_t*>(&sm.Wlo[off]);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vf[ks][nt], d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vf[ks][nt], d, 0, 0, 0);
-            }
-            st[nt] = d;
-        }
-    };
-
-    // y^T tiles: carry term then the intra-chunk product; staged into Vw (bf16).
-    auto output = [&](const f32x4_t (&st)[NTW], const bf16x8_t (&vf)[C::KS][NTW]) {
-        // State fragments as the A operand of the carry product.  The K axis
-        // holds (state row, hi/lo half) pairs: lane (g, col) supplies the bf16
-        // hi parts of its state rows 4g..4g+3 in elements 0..3 and the lo parts
-        // in elements 4..7; the B operand repeats the matching carry-matrix
-        // entries in both halves.
-        bf16x8_t sf[NTW];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            u16x8_t raw;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = st[nt][i];
-                const uint16_t hb = f32_to_bf16(x);
-                raw[i] = hb;
-                raw[4 + i] = f32_to_bf16(x - bf16_to_f32(hb));
-            }
-            sf[nt] = __builtin_bit_cast(bf16x8_t, raw);
-        }
-        constexpr int qu = C::QU;
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-            const int tr = mt * 16 + col;          // position (row of G, A) owned by this lane
-            const u16x4_t a4 = *reinterpret_cast<const u16x4_t*>(&sm.A[tr * 16 + ((g ^ ((tr >> 2) & 3)) * 4)]);
-            const bf16x8_t af =
-                __builtin_bit_cast(bf16x8_t, u16x8_t{a4[0], a4[1], a4[2], a4[3], a4[0], a4[1], a4[2], a4[3]});
-            f32x4_t acc[NTW];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[nt], af, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            const int nks = mt / 2 + 1;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                if (ks < nks) {
-                    const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(
-                        &sm.G[tr * LC + (((4 * ks + g) ^ (tr & C::GSWZ)) * 8)]);
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks][nt], gf, acc[nt], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) {
+                    const float x = bb[e] * bf16_to_f32(vfr[nt][e]);
+                    const uint16_t hb = f32_to_bf16(x);
+                    bv[nt][e] = hb;
+                    bl[nt][e] = f32_to_bf16(x - bf16_to_f32(hb));
                 }
             }
-            // lane holds y(t = tr, p = 16nt + 4g + i), i = 0..3
-            const float grv = sm.gr[tr];
-            const int yswz = (tr / C::YROWS128) & (qu - 1);
+            if (out) {
+                const float sc = sg.ag[T0 + col];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(cat8(bv[nt], hi4(st[nt]))), by,
+                                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    stage_y(T, nt, acc, sc);
+                }
+            }
+            const float at = bk.x;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const uint16_t h0 = f32_to_bf16(acc[nt][0] * grv);
-                const uint16_t h1 = f32_to_bf16(acc[nt][1] * grv);
-                const uint16_t h2 = f32_to_bf16(acc[nt][2] * grv);
-                const uint16_t h3 = f32_to_bf16(acc[nt][3] * grv);
-                const int q = (nt * 4 + g) ^ yswz;
-                *reinterpret_cast<uint2*>(&Vw[tr * WCOLS + q * 4]) = make_uint2(pack2(h0, h1), pack2(h2, h3));
+                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, to_bf16x8(cat8(bv[nt], bv[nt])),
+                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, to_bf16x8(cat8(bl[nt], bl[nt])), mv, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float lr = l16[i], li = l16[i + 1];
+                    const float hr = st[nt][i], hi = st[nt][i + 1];
+                    st[nt][i] = at * (lr * hr - li * hi + mv[i]);
+                    st[nt][i + 1] = at * (li * hr + lr * hi + mv[i + 1]);
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[i] = at * l16[i];
+        } else {
+            // exact path (ragged sub-block, or a clock span too large to factor):
+            // operands evaluated per element from the clock sums.
+            const int T1 = min(T0 + 15, n - 1);
+            const float qp = T0 > 0 ? sg.q2[T0 - 1] : 0.f;
+            const float qe = sg.q2[T1];
+            if (out) {
+                const int t = T0 + col;
+                const float qt = sg.q2[t];
+                const float ea = exp2f(qp - qt);
+                u16x8_t h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sl = 4 * g + e;
+                    float val = 0.f;
+                    if (sl <= col) val = exp2f(sg.q2[T0 + sl] - qt) * sg.gw[T0 + sl] * sm.psi[col - sl];
+                    h[e] = f32_to_bf16(val);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i, j = row >> 1;
+                    float val = 0.f;
+                    if (j < M) {
+                        const float2 cp = sm.cpw[col + 1][j < M ? j : 0];
+                        val = ea * ((row & 1) ? -cp.y : cp.x);
+                    }
+                    h[4 + i] = f32_to_bf16(val);
+                }
+                const bf16x8_t bx = to_bf16x8(h);
+                const float sc = sg.gr[t];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(cat8(vfr[nt], hi4(st[nt]))), bx,
+                                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    stage_y(T, nt, acc, sc);
+                }
+            }
+            // W[row = col][s] = {Re,Im}(lambda_j^{T1-s}) e^{-(qh(T1)-qh(s))} g_w(s), hi + lo
+            u16x8_t w;
+            {
+                const int jr = col >> 1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = T0 + 4 * g + e;
+                    float val = 0.f;
+                    if (jr < M && s <= T1) {
+                        const float2 pw = sm.pw[T1 - s][jr < M ? jr : 0];
+                        val = ((col & 1) ? pw.y : pw.x) * exp2f(sg.q2[s] - qe) * sg.gw[s];
+                    }
+                    const uint16_t hb = f32_to_bf16(val);
+                    w[e] = hb;
+                    w[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
+                }
+            }
+            const float at = exp2f(qp - qe);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = 2 * g + hh;
+                const float2 pn = j < M ? sm.pw[T1 - T0 + 1][j < M ? j : 0] : make_float2(0.f, 0.f);
+                lam[2 * hh] = at * pn.x;
+                lam[2 * hh + 1] = at * pn.y;
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4_t d;
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float hr = st[nt][i], hi = st[nt][i + 1];
+                    d[i] = lam[i] * hr - lam[i + 1] * hi;
+                    d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
+                }
+                st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(w), to_bf16x8(cat8(vfr[nt], vfr[nt])), d, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            const float ar = tr[i], ai = tr[i + 1];
+            tr[i] = ar * lam[i] - ai * lam[i + 1];
+            tr[i + 1] = ar * lam[i + 1] + ai * lam[i];
         }
     };
 
-    // staged y -> global, 16 bytes per lane (undo the 8-byte unit swizzle)
+    // staged y -> global, 16 bytes per lane (the units this lane loaded v from)
     auto store_y = [&](int t0, int n) {
-        constexpr int qu = C::QU;
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
             const int t = t0 + tr;
-            const int yswz = (tr / C::YROWS128) & (qu - 1);
-            const int q0 = (2 * vunit) ^ yswz;          // physical 8-byte unit of the first half
-            const uint4 raw = *reinterpret_cast<const uint4*>(&Vw[tr * WCOLS + (q0 & ~1) * 4]);
-            uint4 outv = raw;
-            if (q0 & 1) outv = make_uint4(raw.z, raw.w, raw.x, raw.y);
+            const uint4 outv = *reinterpret_cast<const uint4*>(&sg.V[vt_off(tr, (int)(vcol0 >> 3))]);
             if (tr < n) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
                 *reinterpret_cast<uint4*>(yg + off) = outv;
@@ -571,81 +623,119 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
 
     // Entering state of this segment: compose predecessors' messages backwards
-    // until an inclusive state is found (segment 0 always publishes one).
+    // until an inclusive state is found (segment 0 always publishes one).  Wave
+    // 0 polls the flags of up to 64 predecessors at once; once every
+    // predecessor nearer than the nearest inclusive one has its aggregate out,
+    // all of those messages are read (independent loads) and folded in order.
     auto lookback = [&](f32x4_t (&e)[NTW]) {
         float cf[4] = {1.f, 0.f, 1.f, 0.f};   // accumulated transfer of modes 2g, 2g+1
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) e[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int pred = seg - 1; pred >= 0; --pred) {
-            if (tid == 0) {
-                unsigned f = 0;
+        int hi = seg - 1;                     // nearest predecessor not folded yet
+        while (hi >= 0) {
+            if (wave == 0) {
+                const int nwin = min(64, hi + 1);
+                int cnt = 1;
+                bool found = true;
                 int it = 0;
                 for (; it < SPIN_LIMIT; ++it) {
-                    f = ld_agent_u(&plan.flags[slot + pred]);
-                    if ((f & ~3u) == tag && (f & 3u) != 0) break;
+                    const unsigned f = lane < nwin ? ld_agent_u(&plan.flags[slot + hi - lane]) : 0u;
+                    const bool ready = (f & ~3u) == tag && (f & 3u) != 0;
+                    const unsigned long long minc = __ballot(ready && (f & 3u) == FLAG_INCL);
+                    const unsigned long long mrdy = __ballot(ready);
+                    found = minc != 0ull;
+                    cnt = found ? __ffsll((long long)minc) : nwin;   // predecessors to fold
+                    const unsigned long long need = cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull);
+                    if ((mrdy & need) == need) break;
                     __builtin_amdgcn_s_sleep(2);
                 }
                 if (it == SPIN_LIMIT) {
-                    __hip_atomic_fetch_or(&plan.hdr[SCAN_HDR_ERROR], SCAN_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-                    f = tag | FLAG_INCL;   // give up: treat the (unwritten) state as final
+                    if (lane == 0)
+                        __hip_atomic_fetch_or(&plan.hdr[SCAN_HDR_ERROR], SCAN_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    cnt = 1;        // give up: treat the (unwritten) nearest state as final
+                    found = true;
                 }
-                sm.flag = f;
+                if (lane == 0) {
+                    sm.lb_cnt = cnt;
+                    sm.lb_found = found ? 1 : 0;
+                }
             }
             __syncthreads();
-            const unsigned f = sm.flag;
-            __syncthreads();   // sm.flag may be rewritten by the next poll
-            const bool incl = (f & 3u) == FLAG_INCL;
-            const float* src = (incl ? plan.incl : plan.agg) + (slot + pred) * (size_t)ROWS * P;
+            const int cnt = sm.lb_cnt;
+            const bool found = sm.lb_found != 0;
+            __syncthreads();   // sm.lb_* may be rewritten by the next window
+            for (int l0 = 0; l0 < cnt; l0 += 2) {
+                float sv[2][NTW][4], lv[2][4];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int p = wave * WCOLS + nt * 16 + col;
+                for (int u = 0; u < 2; ++u) {
+                    const int l = l0 + u;
+                    if (l >= cnt) break;
+                    const int pred = hi - l;
+                    const bool incl = found && l == cnt - 1;
+                    const float* src = (incl ? plan.incl : plan.agg) + (slot + pred) * (size_t)ROWS * P;
 #pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const int row = 4 * g + i;
-                    if (row < ROWS) {
-                        const float sr = ld_agent(&src[(size_t)row * P + p]);
-                        const float si = ld_agent(&src[(size_t)(row + 1) * P + p]);
-                        e[nt][i] += cf[i] * sr - cf[i + 1] * si;
-                        e[nt][i + 1] += cf[i] * si + cf[i + 1] * sr;
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        const int p = wave * WCOLS + nt * 16 + col;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 4 * g + i;
+                            sv[u][nt][i] = row < ROWS ? ld_agent(&src[(size_t)row * P + p]) : 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * g + i;
+                        lv[u][i] = (!incl && row < ROWS) ? ld_agent(&plan.lam[(slot + pred) * ROWS + row]) : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (l0 + u >= cnt) break;
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+                        for (int i = 0; i < 4; i += 2) {
+                            const float sr = sv[u][nt][i], si = sv[u][nt][i + 1];
+                            e[nt][i] += cf[i] * sr - cf[i + 1] * si;
+                            e[nt][i + 1] += cf[i] * si + cf[i + 1] * sr;
+                        }
+                    }
+                    // compose with this predecessor's transfer: cf <- cf * Lambda_pred
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const float ar = cf[i], ai = cf[i + 1];
+                        cf[i] = ar * lv[u][i] - ai * lv[u][i + 1];
+                        cf[i + 1] = ar * lv[u][i + 1] + ai * lv[u][i];
                     }
                 }
             }
-            if (incl) break;
-            // compose with the predecessor's transfer: cf <- cf * Lambda_pred
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const int row = 4 * g + i;
-                float lr = 0.f, li = 0.f;
-                if (row < ROWS) {
-                    lr = ld_agent(&plan.lam[(slot + pred) * ROWS + row]);
-                    li = ld_agent(&plan.lam[(slot + pred) * ROWS + row + 1]);
-                }
-                const float ar = cf[i], ai = cf[i + 1];
-                cf[i] = ar * lr - ai * li;
-                cf[i + 1] = ar * li + ai * lr;
-            }
+            if (found) break;
+            hi -= cnt;
         }
     };
 
-    // ---- sweep 1 (segmented scan only): aggregate of this segment ----------------------
-    f32x4_t st[NTW];
+    // ---- the two sweeps -------------------------------------------------------------------------
+    // Sweep 1 (segmented scan, segments with a successor): the end state from a
+    // zero entering state, or the true one for segment 0.  Sweep 2: outputs.
+    // Each chunk step stages the chunk held in the register buffer and refills
+    // it with the loads of the next chunk, which then overlap the arithmetic.
     const bool has_succ = SEG && seg + 1 < nseg;
-    if (c_begin < c_end) load_chunk(c_begin);
-    if (has_succ) {
-        float tr[4] = {1.f, 0.f, 1.f, 0.f};
+
+    f32x4_t st[NTW];
+    float tr[4] = {1.f, 0.f, 1.f, 0.f};
+    if (SEG && !has_succ && seg > 0) {
+        // last segment: no successor needs an aggregate; only the entering state
+        f32x4_t e[NTW];
+        lookback(e);
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];   // segment 0: its inclusive state directly
-        for (int c = c_begin; c < c_end; ++c) {
-            const int n = min(LC, L - c * LC);
-            // prefetch: next chunk of this sweep, else the first chunk of sweep 2
-            stage_chunk(c + 1 < c_end ? c + 1 : c_begin);
-            build_W(n);
-            __syncthreads();
-            bf16x8_t vf[C::KS][NTW];
-            load_vf(vf);
-            state_update(st, vf, n, tr);
-        }
+        for (int nt = 0; nt < NTW; ++nt) st_in[nt] = e[nt];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];   // segment 0: from state_in; others: zero
+
+    // end of sweep 1: publish, look back, restart from the true entering state
+    auto between_sweeps = [&]() {
         if (seg == 0) {
             publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
         } else {
@@ -664,33 +754,29 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 st_in[nt] = e[nt];
                 st[nt] = inc;
             }
-            __syncthreads();
             publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
         }
-    } else if (SEG && seg > 0) {
-        // last segment: no successor needs an aggregate; only the entering state
-        f32x4_t e[NTW];
-        lookback(e);
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st_in[nt] = e[nt];
-    }
+        for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];
+    };
 
-    // ---- sweep 2: outputs ------------------------------------------------------------------
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];
+    ChunkRegs rb;
+    load_chunk(rb, c_begin);
+    if (has_succ) {
+        for (int c = c_begin; c < c_end; ++c) {
+            const int n = min(LC, L - c * LC);
+            stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
+            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, false, tr);
+        }
+        // no loads are in flight across the look-back (it needs the registers)
+        between_sweeps();
+        load_chunk(rb, c_begin);
+    }
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * LC;
         const int n = min(LC, L - t0);
-        stage_chunk(c + 1 < c_end ? c + 1 : -1);
-        build_G();
-        build_W(n);
-        build_A();
-        __syncthreads();
-        bf16x8_t vf[C::KS][NTW];
-        load_vf(vf);
-        output(st, vf);
-        float tr[4] = {1.f, 0.f, 1.f, 0.f};
-        state_update(st, vf, n, tr);
+        stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
+        for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
         store_y(t0, n);
     }
 
@@ -802,12 +888,17 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc) {
     return p;
 }
 
-size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc) {
-    const ScanPlan p = plan_chunked(B, L, K_T, m, P, Lc);
+size_t lookback_bytes(const ScanPlan& p, int m, int P) {
     if (p.nseg <= 1) return 0;
     const size_t slots = (size_t)p.nseq * p.nseg;
     return align256(SCAN_HDR_WORDS * sizeof(unsigned)) + align256(slots * sizeof(unsigned)) +
            align256(slots * 2 * m * sizeof(float)) + 2 * align256(slots * 2 * (size_t)m * P * sizeof(float));
+}
+
+size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc) {
+    const ScanPlan p = plan_chunked(B, L, K_T, m, P, Lc);
+    if (p.nblocks == 0) return 0;
+    return lookback_bytes(p, m, P);
 }
 
 void bind_workspace(ScanPlan& p, void* ws, int m, int P) {
