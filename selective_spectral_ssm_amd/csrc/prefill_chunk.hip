@@ -164,8 +164,18 @@ __device__ __forceinline__ void st_agent_u(unsigned* p, unsigned x) {
 }
 
 __device__ __forceinline__ bf16x8_t to_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
-__device__ __forceinline__ u16x8_t cat8(u16x4_t a, u16x4_t b) {
-    return u16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Two fp32 values -> one dword of two bf16 (round to nearest even), element 0 low.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+// The low / high bf16 of a dword, exactly, as fp32.
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Eight bf16 MFMA operand slots from two 4-slot halves.
+__device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
 }
 
 template <class C, bool SEG>
@@ -423,72 +433,70 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // of 16 lanes, ds_read_b64_tr_b16 returns to lane i, element e, the (i%4)-th
     // 16-bit value at the address of lane 4e + i/4; so lane (g, col) supplies
     // the address of row T0 + 4g + col/4, columns 4*(col%4) .. +3 of the tile.
-    auto load_vfrag = [&](int T, int nt) -> u16x4_t {
-        const int r = T * 16 + 4 * g + (col >> 2);
+    // The swizzle repeats every 8 rows, so sub-block T is 16*T rows further.
+    int vf_off[NTW], ys_off[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
         const int p0 = wave * WCOLS + nt * 16 + 4 * (col & 3);
-        const int off = vt_off(r, p0 >> 3) + (p0 & 7);
-        const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sg.V[off]));
-        return __builtin_bit_cast(u16x4_t, x);
+        vf_off[nt] = vt_off(4 * g + (col >> 2), p0 >> 3) + (p0 & 7);
+        const int p1 = wave * WCOLS + nt * 16 + 4 * g;
+        ys_off[nt] = vt_off(col, p1 >> 3) + (p1 & 7);
+    }
+    auto load_vfrag = [&](int T, int nt) -> uint2 {
+        const s16x4_t x =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sg.V[vf_off[nt] + T * 16 * P]));
+        return __builtin_bit_cast(uint2, x);
     };
 
-    // y tile of sub-block T (lane holds y(t = T0+col, p0 + i), i < 4) -> staged in
-    // the v tile in place: each wave overwrites only its own columns of rows it
-    // has already read.
+    // y tile of sub-block T (lane holds y(t = T0+col, p1 + i), i < 4, p1 =
+    // wave*WCOLS + nt*16 + 4g) -> staged in the v tile in place: each wave
+    // overwrites only its own columns of rows it has already read.
     auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) {
-        const int t = T * 16 + col;
-        const int p0 = wave * WCOLS + nt * 16 + 4 * g;
-        const uint16_t h0 = f32_to_bf16(acc[0] * scale);
-        const uint16_t h1 = f32_to_bf16(acc[1] * scale);
-        const uint16_t h2 = f32_to_bf16(acc[2] * scale);
-        const uint16_t h3 = f32_to_bf16(acc[3] * scale);
-        *reinterpret_cast<uint2*>(&sg.V[vt_off(t, p0 >> 3) + (p0 & 7)]) = make_uint2(pack2(h0, h1), pack2(h2, h3));
+        *reinterpret_cast<uint2*>(&sg.V[ys_off[nt] + T * 16 * P]) =
+            make_uint2(pk_bf16(acc[0] * scale, acc[1] * scale), pk_bf16(acc[2] * scale, acc[3] * scale));
     };
 
-    auto hi4 = [&](const f32x4_t& x) -> u16x4_t {
-        return u16x4_t{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
-    };
+    auto hi4 = [&](const f32x4_t& x) -> uint2 { return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])); };
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
     auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4]) {
         const int T0 = T * 16;
         const float2 bk = sg.blk[T];
-        u16x4_t vfr[NTW];
+        uint2 vfr[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) vfr[nt] = load_vfrag(T, nt);
         float lam[4];   // Lambda_T for modes 2g, 2g+1
         if (bk.y == 0.f) {
-            // factored path: scale v by b(s), constant operands
+            // factored path: scale v by b(s), constant operands.  b(s) v(s) is
+            // split into bf16 hi + lo: the output product uses hi, the state
+            // product both, so the state keeps ~16 mantissa bits.
             const float4 b4 = *reinterpret_cast<const float4*>(&sg.bq[T0 + 4 * g]);
-            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-            // b(s) v(s) split into bf16 hi + lo: the output product uses hi, the
-            // state product both, so the state keeps ~16 mantissa bits.
-            u16x4_t bv[NTW], bl[NTW];
+            uint2 bv[NTW], bl[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = bb[e] * bf16_to_f32(vfr[nt][e]);
-                    const uint16_t hb = f32_to_bf16(x);
-                    bv[nt][e] = hb;
-                    bl[nt][e] = f32_to_bf16(x - bf16_to_f32(hb));
-                }
+                const float x0 = b4.x * lo_f32(vfr[nt].x), x1 = b4.y * hi_f32(vfr[nt].x);
+                const float x2 = b4.z * lo_f32(vfr[nt].y), x3 = b4.w * hi_f32(vfr[nt].y);
+                const uint32_t h01 = pk_bf16(x0, x1), h23 = pk_bf16(x2, x3);
+                bv[nt] = make_uint2(h01, h23);
+                bl[nt] = make_uint2(pk_bf16(x0 - lo_f32(h01), x1 - hi_f32(h01)),
+                                    pk_bf16(x2 - lo_f32(h23), x3 - hi_f32(h23)));
             }
             if (out) {
                 const float sc = sg.ag[T0 + col];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(cat8(bv[nt], hi4(st[nt]))), by,
-                                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(bv[nt], hi4(st[nt])), by, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     stage_y(T, nt, acc, sc);
                 }
             }
             const float at = bk.x;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, to_bf16x8(cat8(bv[nt], bv[nt])),
+                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
                                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, to_bf16x8(cat8(bl[nt], bl[nt])), mv, 0, 0, 0);
+                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bl[nt], bl[nt]), mv, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
                     const float lr = l16[i], li = l16[i + 1];
@@ -509,13 +517,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int t = T0 + col;
                 const float qt = sg.q2[t];
                 const float ea = exp2f(qp - qt);
-                u16x8_t h;
+                float gv[4], av[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sl = 4 * g + e;
-                    float val = 0.f;
-                    if (sl <= col) val = exp2f(sg.q2[T0 + sl] - qt) * sg.gw[T0 + sl] * sm.psi[col - sl];
-                    h[e] = f32_to_bf16(val);
+                    gv[e] = sl <= col ? exp2f(sg.q2[T0 + sl] - qt) * sg.gw[T0 + sl] * sm.psi[col - sl] : 0.f;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -525,19 +531,20 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                         const float2 cp = sm.cpw[col + 1][j < M ? j : 0];
                         val = ea * ((row & 1) ? -cp.y : cp.x);
                     }
-                    h[4 + i] = f32_to_bf16(val);
+                    av[i] = val;
                 }
-                const bf16x8_t bx = to_bf16x8(h);
+                const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
+                                              make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
                 const float sc = sg.gr[t];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(cat8(vfr[nt], hi4(st[nt]))), bx,
-                                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     stage_y(T, nt, acc, sc);
                 }
             }
             // W[row = col][s] = {Re,Im}(lambda_j^{T1-s}) e^{-(qh(T1)-qh(s))} g_w(s), hi + lo
-            u16x8_t w;
+            float wv[4];
             {
                 const int jr = col >> 1;
 #pragma unroll
@@ -548,11 +555,13 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                         const float2 pw = sm.pw[T1 - s][jr < M ? jr : 0];
                         val = ((col & 1) ? pw.y : pw.x) * exp2f(sg.q2[s] - qe) * sg.gw[s];
                     }
-                    const uint16_t hb = f32_to_bf16(val);
-                    w[e] = hb;
-                    w[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
+                    wv[e] = val;
                 }
             }
+            const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
+            const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
+                                          make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
+                                                     pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
             const float at = exp2f(qp - qe);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -570,7 +579,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     d[i] = lam[i] * hr - lam[i + 1] * hi;
                     d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
                 }
-                st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(w), to_bf16x8(cat8(vfr[nt], vfr[nt])), d, 0, 0, 0);
+                st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
             }
         }
 #pragma unroll
@@ -870,11 +879,14 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc) {
     p.nseq = B * K_T;
     p.nchunks = (L + Lc - 1) / Lc;
     if (p.nseq == 0 || p.nchunks == 0) return p;
-    // Enough workgroups to fill 256 CUs several times over: sequences alone when
-    // there are plenty of them, otherwise segments of at least two chunks.
-    constexpr int TARGET_BLOCKS = 2048;
+    // With about 1.5 sequences per CU or more, whole sequences keep the GPU
+    // busy and the segmented scan's extra sweep would only cost time.  Below
+    // that, cut sequences into segments of at least two chunks, aiming at
+    // about 16 workgroups per CU so that the look-back chains overlap.
+    constexpr int SEQ_ENOUGH = 384;
+    constexpr int TARGET_BLOCKS = 4096;
     int seg_chunks = p.nchunks;
-    if (p.nseq < TARGET_BLOCKS) {
+    if (p.nseq < SEQ_ENOUGH) {
         const int want_seg = (TARGET_BLOCKS + p.nseq - 1) / p.nseq;
         seg_chunks = (p.nchunks + want_seg - 1) / want_seg;
         if (seg_chunks < 2) seg_chunks = 2;
