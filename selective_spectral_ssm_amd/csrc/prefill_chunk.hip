@@ -67,6 +67,7 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float LOG2E = 1.4426950408889634f;
 // Largest clock span of a sub-block, in log2 units, that the factored path
@@ -80,6 +81,17 @@ constexpr unsigned FLAG_INCL = 2u;   // inclusive state (true state after the se
 // plus a short sleep, so this is tens of milliseconds); exceeding it records
 // SCAN_ERR_TIMEOUT in the workspace header instead of waiting forever.
 constexpr int SPIN_LIMIT = 1 << 16;
+
+}  // namespace
+
+// Bytes of one staged chunk (v tile and per-position factors) and the number
+// of chunks a segment keeps resident in LDS (a budget of 40 KB per workgroup).
+constexpr int stage_bytes(int P, int LC) { return LC * P * 2 + 5 * LC * 4 + (LC / 16) * 8; }
+constexpr int resident_chunks(int P, int LC) {
+    return 40960 / stage_bytes(P, LC) < 1 ? 1 : (40960 / stage_bytes(P, LC) > 4 ? 4 : 40960 / stage_bytes(P, LC));
+}
+
+namespace {
 
 template <int P_, int M_, int LC_>
 struct Cfg {
@@ -99,6 +111,8 @@ struct Cfg {
     // 16 rows a transposing fragment read touches over all LDS banks.
     static constexpr int RP256 = P >= 128 ? 1 : 128 / P;   // rows per 256 bytes
     static constexpr int SWZ_MASK = P / 16 - 1;
+    // chunks of a segment kept resident in LDS between the two sweeps
+    static constexpr int RES = resident_chunks(P, LC);
     static_assert(P % 16 == 0 && NT % NW == 0, "P must be 16, 32, 64 or 128");
     static_assert(LC % 32 == 0 && LC <= 128, "chunk length must be 32, 64 or 128");
     static_assert(M >= 1 && M <= 8, "1..8 modes");
@@ -119,7 +133,7 @@ struct __align__(16) Stage {
 
 template <class C>
 struct __align__(16) Smem {
-    Stage<C> stg;
+    Stage<C> stg[C::RES];
     float2 pw[17][C::M];             // lambda_j^tau, tau = 0..16
     float2 cpw[17][C::M];            // c_j lambda_j^tau
     float psi[16];                   // sum_j Re(c_j lambda_j^tau), tau = 0..15
@@ -237,6 +251,49 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const uint16_t* grg = static_cast<const uint16_t*>(a.g_r);
     uint16_t* yg = static_cast<uint16_t*>(a.y);
 
+    // ---- segmented scan: every chunk of the segment is requested at once -------------------
+    // v tiles go straight into their LDS stage buffers (global_load_lds, 16
+    // bytes per lane; a wave instruction fills 1 KB of the tile, so each lane
+    // fetches the 16-byte unit whose swizzled slot is lane-th of that block),
+    // the controls into wave 0's registers.  These loads overlap the pole
+    // tables below and, for the last segment, the look-back.
+    float ecd[C::RES][C::CPL], ecw[C::RES][C::CPL], ecr[C::RES][C::CPL];
+    if (SEG) {
+        constexpr int UPR = P / 8;                 // 16-byte units per tile row
+        constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
+        const int nck = c_end - c_begin;
+#pragma unroll
+        for (int i = 0; i < C::RES; ++i) {
+            if (i < nck) {
+                for (int ins = wave; ins < INSTR; ins += C::NW) {
+                    const int sl = ins * 64 + lane;
+                    const int r = sl / UPR, pu = sl - r * UPR;
+                    const int u = pu ^ (((r / C::RP256) & C::SWZ_MASK) << 1);
+                    const int t = min((c_begin + i) * LC + r, L - 1);   // rows past L: any valid row
+                    const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&sm.stg[i].V[ins * 512]), 16, 0, 0);
+                }
+                if (wave == 0) {
+#pragma unroll
+                    for (int u = 0; u < C::CPL; ++u) {
+                        const int rr = lane * C::CPL + u;
+                        const int t = (c_begin + i) * LC + rr;
+                        if (rr < LC && t < L) {
+                            const size_t row = ((size_t)b * L + t) * K + k;
+                            ecd[i][u] = a.delta[row];
+                            ecw[i][u] = bf16_to_f32(gwg[row]);
+                            ecr[i][u] = bf16_to_f32(grg[row]);
+                        } else {
+                            ecd[i][u] = 0.f;
+                            ecw[i][u] = 0.f;
+                            ecr[i][u] = 0.f;
+                        }
+                    }
+                }
+            }
+        }
+    }
+
     // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16 ------------------------
     for (int idx = tid; idx < 17 * M; idx += C::THREADS) {
         const int tau = idx / M, j = idx - tau * M;
@@ -329,7 +386,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const int vrow_l = lane / C::LPR;          // row of this lane inside a wave load
     const int vunit = lane % C::LPR;           // 16-byte unit of this lane inside a row
     const size_t vcol0 = (size_t)wave * WCOLS + vunit * 8;
-    Stage<C>& sg = sm.stg;
+    Stage<C>* sgp = &sm.stg[0];   // staged chunk the helpers work on
     // element offset of (row r, first column of 16-byte unit u) in the v tile
     auto vt_off = [&](int r, int u) { return r * P + ((u ^ (((r / C::RP256) & C::SWZ_MASK) << 1)) << 3); };
 
@@ -370,24 +427,15 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     };
 
-    // v tile and controls of the loaded chunk (n valid positions) -> LDS, then the
-    // loads of chunk `next` (if >= 0) are issued so that they overlap this chunk's
-    // arithmetic.  Wave 0 scans the clock it holds and derives the per-position
-    // factors b(s), a(t) g_r(t) and the per-sub-block A_T.  Starts and ends with
-    // a barrier.
-    auto stage_chunk = [&](ChunkRegs& rg, int n, int next) {
-        __syncthreads();   // previous readers of the staged chunk are done
-#pragma unroll
-        for (int i = 0; i < C::NLD; ++i) {
-            const int tr = i * C::RPI + vrow_l;
-            *reinterpret_cast<uint4*>(&sg.V[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
-        }
+    // Wave 0: clock sums and per-position factors of the staged chunk (n valid
+    // positions) from the controls it holds.
+    auto stage_ctrl = [&](const float (&cd)[C::CPL], const float (&cw)[C::CPL], const float (&cr)[C::CPL], int n) {
         if (wave == 0) {
             float loc[C::CPL];
             float run = 0.f;
 #pragma unroll
             for (int u = 0; u < C::CPL; ++u) {
-                run += rg.cd[u];
+                run += cd[u];
                 loc[u] = run;
             }
             float incl = run;
@@ -401,9 +449,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int u = 0; u < C::CPL; ++u) {
                 const int idx = lane * C::CPL + u;
                 if (idx < LC) {
-                    sg.q2[idx] = (excl + loc[u]) * LOG2E;
-                    sg.gw[idx] = rg.cw[u];
-                    sg.gr[idx] = rg.cr[u];
+                    sgp->q2[idx] = (excl + loc[u]) * LOG2E;
+                    sgp->gw[idx] = cw[u];
+                    sgp->gr[idx] = cr[u];
                 }
             }
             // same wave: its own LDS writes above are visible to these reads
@@ -412,18 +460,31 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int idx = lane * C::CPL + u;
                 if (idx < LC) {
                     const int T0 = idx & ~15;
-                    const float qp = T0 > 0 ? sg.q2[T0 - 1] : 0.f;
-                    const float q = sg.q2[idx];
-                    sg.bq[idx] = idx < n ? exp2f(q - qp) * rg.cw[u] : 0.f;
-                    sg.ag[idx] = exp2f(qp - q) * rg.cr[u];
+                    const float qp = T0 > 0 ? sgp->q2[T0 - 1] : 0.f;
+                    const float q = sgp->q2[idx];
+                    sgp->bq[idx] = idx < n ? exp2f(q - qp) * cw[u] : 0.f;
+                    sgp->ag[idx] = exp2f(qp - q) * cr[u];
                     const int T1 = min(T0 + 15, n - 1);
                     if (idx == T1) {
                         const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
-                        sg.blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
+                        sgp->blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
                     }
                 }
             }
         }
+    };
+
+    // Register path: v tile and controls of the loaded chunk -> LDS, then the
+    // loads of chunk `next` (if >= 0) are issued so that they overlap this
+    // chunk's arithmetic.  Starts and ends with a barrier.
+    auto stage_chunk = [&](ChunkRegs& rg, int n, int next) {
+        __syncthreads();   // previous readers of the staged chunk are done
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) {
+            const int tr = i * C::RPI + vrow_l;
+            *reinterpret_cast<uint4*>(&sgp->V[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
+        }
+        stage_ctrl(rg.cd, rg.cw, rg.cr, n);
         if (next >= 0) load_chunk(rg, next);
         __syncthreads();
     };
@@ -444,7 +505,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     }
     auto load_vfrag = [&](int T, int nt) -> uint2 {
         const s16x4_t x =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sg.V[vf_off[nt] + T * 16 * P]));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sgp->V[vf_off[nt] + T * 16 * P]));
         return __builtin_bit_cast(uint2, x);
     };
 
@@ -452,7 +513,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // wave*WCOLS + nt*16 + 4g) -> staged in the v tile in place: each wave
     // overwrites only its own columns of rows it has already read.
     auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) {
-        *reinterpret_cast<uint2*>(&sg.V[ys_off[nt] + T * 16 * P]) =
+        *reinterpret_cast<uint2*>(&sgp->V[ys_off[nt] + T * 16 * P]) =
             make_uint2(pk_bf16(acc[0] * scale, acc[1] * scale), pk_bf16(acc[2] * scale, acc[3] * scale));
     };
 
@@ -462,7 +523,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
     auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4]) {
         const int T0 = T * 16;
-        const float2 bk = sg.blk[T];
+        const float2 bk = sgp->blk[T];
         uint2 vfr[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) vfr[nt] = load_vfrag(T, nt);
@@ -471,7 +532,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             // factored path: scale v by b(s), constant operands.  b(s) v(s) is
             // split into bf16 hi + lo: the output product uses hi, the state
             // product both, so the state keeps ~16 mantissa bits.
-            const float4 b4 = *reinterpret_cast<const float4*>(&sg.bq[T0 + 4 * g]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
             uint2 bv[NTW], bl[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
@@ -483,7 +544,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                                     pk_bf16(x2 - lo_f32(h23), x3 - hi_f32(h23)));
             }
             if (out) {
-                const float sc = sg.ag[T0 + col];
+                const float sc = sgp->ag[T0 + col];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -511,17 +572,17 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             // exact path (ragged sub-block, or a clock span too large to factor):
             // operands evaluated per element from the clock sums.
             const int T1 = min(T0 + 15, n - 1);
-            const float qp = T0 > 0 ? sg.q2[T0 - 1] : 0.f;
-            const float qe = sg.q2[T1];
+            const float qp = T0 > 0 ? sgp->q2[T0 - 1] : 0.f;
+            const float qe = sgp->q2[T1];
             if (out) {
                 const int t = T0 + col;
-                const float qt = sg.q2[t];
+                const float qt = sgp->q2[t];
                 const float ea = exp2f(qp - qt);
                 float gv[4], av[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sl = 4 * g + e;
-                    gv[e] = sl <= col ? exp2f(sg.q2[T0 + sl] - qt) * sg.gw[T0 + sl] * sm.psi[col - sl] : 0.f;
+                    gv[e] = sl <= col ? exp2f(sgp->q2[T0 + sl] - qt) * sgp->gw[T0 + sl] * sm.psi[col - sl] : 0.f;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -535,7 +596,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 }
                 const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
                                               make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
-                const float sc = sg.gr[t];
+                const float sc = sgp->gr[t];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -553,7 +614,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     float val = 0.f;
                     if (jr < M && s <= T1) {
                         const float2 pw = sm.pw[T1 - s][jr < M ? jr : 0];
-                        val = ((col & 1) ? pw.y : pw.x) * exp2f(sg.q2[s] - qe) * sg.gw[s];
+                        val = ((col & 1) ? pw.y : pw.x) * exp2f(sgp->q2[s] - qe) * sgp->gw[s];
                     }
                     wv[e] = val;
                 }
@@ -596,7 +657,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
             const int t = t0 + tr;
-            const uint4 outv = *reinterpret_cast<const uint4*>(&sg.V[vt_off(tr, (int)(vcol0 >> 3))]);
+            const uint4 outv = *reinterpret_cast<const uint4*>(&sgp->V[vt_off(tr, (int)(vcol0 >> 3))]);
             if (tr < n) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
                 *reinterpret_cast<uint4*>(yg + off) = outv;
@@ -733,13 +794,6 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 
     f32x4_t st[NTW];
     float tr[4] = {1.f, 0.f, 1.f, 0.f};
-    if (SEG && !has_succ && seg > 0) {
-        // last segment: no successor needs an aggregate; only the entering state
-        f32x4_t e[NTW];
-        lookback(e);
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st_in[nt] = e[nt];
-    }
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];   // segment 0: from state_in; others: zero
 
@@ -770,23 +824,53 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
 
     ChunkRegs rb;
-    load_chunk(rb, c_begin);
-    if (has_succ) {
-        for (int c = c_begin; c < c_end; ++c) {
-            const int n = min(LC, L - c * LC);
-            stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
-            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, false, tr);
+    if (SEG) {
+        // Segment: its (at most RES) chunks were requested up front and stay in LDS.
+        const int nck = c_end - c_begin;
+        if (!has_succ && seg > 0) {
+            // last segment: only the entering state is needed
+            f32x4_t e[NTW];
+            lookback(e);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt] = e[nt];
         }
-        // no loads are in flight across the look-back (it needs the registers)
-        between_sweeps();
+        wait_stores_complete();   // this wave's tile loads have landed
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < C::RES; ++i) {
+            if (i < nck) {
+                sgp = &sm.stg[i];
+                stage_ctrl(ecd[i], ecw[i], ecr[i], min(LC, L - (c_begin + i) * LC));
+            }
+        }
+        __syncthreads();
+        if (has_succ) {
+            for (int i = 0; i < nck; ++i) {
+                const int n = min(LC, L - (c_begin + i) * LC);
+                sgp = &sm.stg[i];
+                for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, false, tr);
+            }
+            between_sweeps();
+        }
+        // sweep 2 from the resident chunks: each wave reads and overwrites only
+        // its own columns, so no barrier is needed between chunks
+        for (int i = 0; i < nck; ++i) {
+            const int t0 = (c_begin + i) * LC;
+            const int n = min(LC, L - t0);
+            sgp = &sm.stg[i];
+            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
+            store_y(t0, n);
+        }
+    } else {
+        // whole sequence, streamed through one staging buffer
         load_chunk(rb, c_begin);
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-        const int t0 = c * LC;
-        const int n = min(LC, L - t0);
-        stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
-        for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
-        store_y(t0, n);
+        for (int c = c_begin; c < c_end; ++c) {
+            const int t0 = c * LC;
+            const int n = min(LC, L - t0);
+            stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
+            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
+            store_y(t0, n);
+        }
     }
 
     // ---- leaving state ----------------------------------------------------------------------
@@ -880,22 +964,15 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc) {
     p.nchunks = (L + Lc - 1) / Lc;
     if (p.nseq == 0 || p.nchunks == 0) return p;
     // With about 1.5 sequences per CU or more, whole sequences keep the GPU
-    // busy and the segmented scan's extra sweep would only cost time.  Below
-    // that, cut sequences into segments of at least two chunks, aiming at
-    // about 16 workgroups per CU so that the look-back chains overlap.
+    // busy.  Below that, sequences are cut into segments of as many chunks as
+    // a workgroup keeps resident in LDS, so that v is read from memory once.
     constexpr int SEQ_ENOUGH = 384;
-    constexpr int TARGET_BLOCKS = 4096;
     int seg_chunks = p.nchunks;
-    if (p.nseq < SEQ_ENOUGH) {
-        const int want_seg = (TARGET_BLOCKS + p.nseq - 1) / p.nseq;
-        seg_chunks = (p.nchunks + want_seg - 1) / want_seg;
-        if (seg_chunks < 2) seg_chunks = 2;
-        if (seg_chunks > p.nchunks) seg_chunks = p.nchunks;
-    }
+    if (p.nseq < SEQ_ENOUGH) seg_chunks = resident_chunks(P, Lc);
+    if (seg_chunks > p.nchunks) seg_chunks = p.nchunks;
     p.seg_chunks = seg_chunks;
     p.nseg = (p.nchunks + seg_chunks - 1) / seg_chunks;
     p.nblocks = p.nseq * p.nseg;
-    (void)P;
     (void)m;
     return p;
 }
