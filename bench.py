@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -29,6 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 SLEEP_CYCLES = 200_000_000
+# HBM bytes per launch of the main prefill kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by the same counters on a plain copy of known size.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_chunk_mixer370m_kt24.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
+                  for f in ("prefill_chunk.hip", "essh_internal.h")]
 METRIC = "selective spectral scan prefill tokens/s + decode µs/step, % of HBM roofline"
 
 
@@ -43,6 +49,45 @@ def to_dev(x):
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch recorded for the current kernel source, else None.
+
+    The counters only describe the kernel they were taken on: when the source
+    hash recorded beside them differs from the current one, traffic is unknown."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy (read N bytes, write N bytes) for the counter calibration."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 launches of neg over {mib} MiB fp32 (reads and writes {n * 4} bytes each)")
 
 
 def time_launches(fn, steps, warmup):
@@ -193,6 +238,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the tier sweeps")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -203,9 +250,12 @@ def main():
     from selective_spectral_ssm_amd import essh, sizes
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     essh.lib()   # fail loudly if the HIP library is not built
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
 
     log("prefill: mixer370m_prefill K_T=24")
     main_res, w, inp = prefill_case(1, 24, args.steps, args.warmup)
+    traffic = measured_traffic()
     res = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -224,7 +274,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel",
                      "achieved": main_res["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": main_res["achieved_GBs"] / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": None if traffic is None else traffic / (main_res["us_per_launch"] * 1e-6) / 1e9,
+                     "traffic_bytes_per_launch": traffic,
                      "alg_bytes_per_launch": main_res["alg_bytes"],
                      "us_per_launch": main_res["us_per_launch"]},
     }
