@@ -9,7 +9,7 @@ full tier K_T=24, inputs resident in HBM.  ``value`` is tokens per second
 (B*L per step).  The same JSON line also carries
   * roofline: algorithmic bytes of one prefill launch / its average duration
     (HIP events around each launch on the launch stream) against 8 TB/s;
-  * cpu_baseline: the CPU oracle (float32 build, OpenMP) on the same workload;
+  * cpu_baseline: the fp64 CPU oracle (OpenMP over sequences) on the same workload;
   * decode: the 24-layer batch-one decode workload (K=32, m=8, P=128, K_T=32),
     1024 steps replayed from a HIP graph, us/step and kernel roofline;
   * extra: tier sweeps of the three prefill workloads.
@@ -88,6 +88,27 @@ def copy_calibration(mib):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"copy calibration: 3 launches of neg over {mib} MiB fp32 (reads and writes {n * 4} bytes each)")
+
+
+def copy_bandwidth(mib=1024, reps=10):
+    """Bytes read + written per second by a plain elementwise copy over mib MiB:
+    the bandwidth an ideal streaming kernel reaches on this device."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    return 2 * n * 4 / sec / 1e9
 
 
 def time_launches(fn, steps, warmup):
@@ -209,25 +230,31 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
                 frac_of_hbm_peak=nbytes / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
-def cpu_baseline(inp, w, K_T, budget_s=10.0):
-    import numpy as np
+def cpu_baseline(inp, w, K_T, budget_s=10.0, max_runs=200):
+    """The fp64 CPU oracle, as the parity tests use it, on the whole main workload.
+
+    The workload takes a small fraction of a second on the host, so the sample
+    is that whole workload repeated for about budget_s seconds; the median run
+    gives the rate."""
     import oracle
     from selective_spectral_ssm_amd.inputs import as_f64
     nthreads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     nthreads = max(1, min(nthreads, 16))
-    x = dict(v=as_f64(inp["v"], w.io).astype(np.float32), delta=inp["delta"],
-             g_w=as_f64(inp["g_w"], w.io).astype(np.float32), g_r=as_f64(inp["g_r"], w.io).astype(np.float32),
-             rho=inp["rho"], theta=inp["theta"], c=inp["c"])
+    x = dict(v=as_f64(inp["v"], w.io), delta=inp["delta"].astype("float64"),
+             g_w=as_f64(inp["g_w"], w.io), g_r=as_f64(inp["g_r"], w.io),
+             rho=inp["rho"].astype("float64"), theta=inp["theta"].astype("float64"),
+             c=inp["c"].astype("float64"))
     times = []
     t_start = time.perf_counter()
-    while len(times) < 5 and (time.perf_counter() - t_start) < budget_s:
+    while len(times) < max_runs and (time.perf_counter() - t_start) < budget_s:
         t0 = time.perf_counter()
-        oracle.prefill_f32(**x, K_T=K_T, nthreads=nthreads)
+        oracle.prefill(**x, K_T=K_T, nthreads=nthreads)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
-    return dict(value=w.B * w.L / med, unit="tokens/s", cores=oracle.threads_used("f32"), kind="oracle",
-                sample=f"whole {w.name} workload (B={w.B}, L={w.L}, K_T={K_T}), float32 oracle build, "
-                       f"median of {len(times)} runs", seconds_per_run=med)
+    return dict(value=w.B * w.L / med, unit="tokens/s", cores=oracle.threads_used("f64"), kind="oracle",
+                sample=f"whole {w.name} workload (B={w.B}, L={w.L}, K_T={K_T}), fp64 oracle, "
+                       f"median of {len(times)} runs over {time.perf_counter() - t_start:.1f} s",
+                seconds_per_run=med)
 
 
 def main():
@@ -256,6 +283,8 @@ def main():
     log("prefill: mixer370m_prefill K_T=24")
     main_res, w, inp = prefill_case(1, 24, args.steps, args.warmup)
     traffic = measured_traffic()
+    copy_gbs = copy_bandwidth()
+    log(f"plain copy: {copy_gbs:.0f} GB/s (read + write)")
     res = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -277,6 +306,7 @@ def main():
                      "traffic": None if traffic is None else traffic / (main_res["us_per_launch"] * 1e-6) / 1e9,
                      "traffic_bytes_per_launch": traffic,
                      "alg_bytes_per_launch": main_res["alg_bytes"],
+                     "copy_GBs": copy_gbs, "frac_of_copy": main_res["achieved_GBs"] / copy_gbs,
                      "us_per_launch": main_res["us_per_launch"]},
     }
     if not args.no_decode:

@@ -113,7 +113,20 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d);
  *                        may alias state_in.  Channels k >= K_T untouched.
  *   y                    [B, L, K, P] output; channels k >= K_T untouched.
  *   workspace            device scratch of at least essh_prefill_workspace_bytes(d)
- *                        bytes (may be NULL if that is 0); 256-byte aligned.
+ *                        bytes (may be NULL if that is 0); 256-byte aligned;
+ *                        owned by the caller.  It holds the look-back records
+ *                        of a segmented scan (used when B * K_T is too small to
+ *                        fill the GPU).  Zero-fill it once before its first
+ *                        use and again whenever it is bound to other dims;
+ *                        every call leaves it ready for the next call with
+ *                        the same dims, so it is not cleared per call (a
+ *                        captured graph replays without a memset).  Calls
+ *                        that share one workspace must be ordered (one
+ *                        stream, or events): concurrent calls on one
+ *                        workspace race.  Every wait inside the scan is
+ *                        bounded; if one ever runs out, the kernel sets
+ *                        32-bit word 1 of the workspace to a nonzero error
+ *                        code and that call's y and state_out are invalid.
  *   stream               HIP stream to enqueue on.
  * y must not overlap any input.  Results do not depend on Lc beyond rounding.
  */
