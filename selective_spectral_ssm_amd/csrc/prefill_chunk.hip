@@ -73,6 +73,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // Largest clock span of a sub-block, in log2 units, that the factored path
 // takes: b(s) <= 2^64 g_w(s) keeps b(s) v(s) far from overflow.
 constexpr float SPAN2_FAST_MAX = 64.f;
+// Largest clock span of a 64-position block, in log2 units, that the block
+// path takes: with the clock referenced to the middle of the block, a(t) and
+// b(s) stay within 2^{+-64}, the same range the sub-block path allows.
+constexpr float SPAN2_BLOCK_MAX = 128.f;
 
 // Look-back flag kinds (low two bits of a flag word; the rest is the epoch tag).
 constexpr unsigned FLAG_AGG = 1u;    // aggregate (end state from a zero entering state) and transfer
@@ -81,12 +85,16 @@ constexpr unsigned FLAG_INCL = 2u;   // inclusive state (true state after the se
 // plus a short sleep, so this is tens of milliseconds); exceeding it records
 // SCAN_ERR_TIMEOUT in the workspace header instead of waiting forever.
 constexpr int SPIN_LIMIT = 1 << 16;
+// s_waitcnt operand: vector memory counter 0, the other counters unconstrained.
+constexpr int WAIT_VMEM0 = 0x0F70;
 
 }  // namespace
 
 // Bytes of one staged chunk (v tile and per-position factors) and the number
 // of chunks a segment keeps resident in LDS (a budget of 40 KB per workgroup).
-constexpr int stage_bytes(int P, int LC) { return LC * P * 2 + 5 * LC * 4 + (LC / 16) * 8; }
+constexpr int stage_bytes(int P, int LC) {
+    return LC * P * 2 + 5 * LC * 4 + (LC / 16) * 8 + (LC >= 64 ? LC / 64 : 1) * 16;
+}
 constexpr int resident_chunks(int P, int LC) {
     return 40960 / stage_bytes(P, LC) < 1 ? 1 : (40960 / stage_bytes(P, LC) > 4 ? 4 : 40960 / stage_bytes(P, LC));
 }
@@ -102,6 +110,11 @@ struct Cfg {
     static constexpr int THREADS = 64 * NW;
     static constexpr int WCOLS = 16 * NTW;          // value columns per wave
     static constexpr int NSB = LC / 16;             // 16-position sub-blocks per chunk
+    // Arithmetic blocks: NB sub-blocks (64 positions, or the whole chunk when
+    // it is shorter) whose state is carried once per block.
+    static constexpr int NB = LC >= 64 ? 4 : LC / 16;
+    static constexpr int BLK = 16 * NB;
+    static constexpr int NBLK = LC / BLK;           // blocks per chunk
     static constexpr int LPR = WCOLS / 8;           // lanes per v row (16 B each)
     static constexpr int RPI = 64 / LPR;            // v rows per wave load
     static constexpr int NLD = LC / RPI;            // wave loads per chunk
@@ -128,6 +141,7 @@ struct __align__(16) Stage {
     float bq[C::LC];                 // b(s) = e^{qh(s)-qh(T0-1)} g_w(s)   (0 beyond the chunk)
     float ag[C::LC];                 // a(t) g_r(t) = e^{-(qh(t)-qh(T0-1))} g_r(t)
     float2 blk[C::NSB];              // per sub-block: (A_T, 1 if the exact path is needed)
+    float4 blkB[C::NBLK];            // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed)
     alignas(16) uint16_t V[C::LC * C::P];   // v tile [t][P] (swizzled units); y staged in place
 };
 
@@ -136,7 +150,8 @@ struct __align__(16) Smem {
     Stage<C> stg[C::RES];
     float2 pw[17][C::M];             // lambda_j^tau, tau = 0..16
     float2 cpw[17][C::M];            // c_j lambda_j^tau
-    float psi[16];                   // sum_j Re(c_j lambda_j^tau), tau = 0..15
+    float2 p16[C::NB + 1][C::M];     // lambda_j^{16 d}, d = 0..NB
+    float psi[C::BLK];               // sum_j Re(c_j lambda_j^tau), tau = 0..BLK-1
     int ticket;
     unsigned epoch;
     int lb_cnt;
@@ -257,7 +272,10 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // fetches the 16-byte unit whose swizzled slot is lane-th of that block),
     // the controls into wave 0's registers.  These loads overlap the pole
     // tables below and, for the last segment, the look-back.
-    float ecd[C::RES][C::CPL], ecw[C::RES][C::CPL], ecr[C::RES][C::CPL];
+    // (gates kept as raw bf16 bits: converting them here would make the wave
+    // wait for these loads, and so for every load issued before them)
+    float ecd[C::RES][C::CPL];
+    uint32_t ecw[C::RES][C::CPL], ecr[C::RES][C::CPL];
     if (SEG) {
         constexpr int UPR = P / 8;                 // 16-byte units per tile row
         constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
@@ -281,12 +299,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                         if (rr < LC && t < L) {
                             const size_t row = ((size_t)b * L + t) * K + k;
                             ecd[i][u] = a.delta[row];
-                            ecw[i][u] = bf16_to_f32(gwg[row]);
-                            ecr[i][u] = bf16_to_f32(grg[row]);
+                            ecw[i][u] = gwg[row];
+                            ecr[i][u] = grg[row];
                         } else {
                             ecd[i][u] = 0.f;
-                            ecw[i][u] = 0.f;
-                            ecr[i][u] = 0.f;
+                            ecw[i][u] = 0u;
+                            ecr[i][u] = 0u;
                         }
                     }
                 }
@@ -294,77 +312,119 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     }
 
-    // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16 ------------------------
-    for (int idx = tid; idx < 17 * M; idx += C::THREADS) {
-        const int tau = idx / M, j = idx - tau * M;
+    // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16, lambda^{16 d} ---------
+    for (int idx = tid; idx < (18 + C::NB) * M; idx += C::THREADS) {
+        const bool blk16 = idx >= 17 * M;
+        const int id2 = blk16 ? idx - 17 * M : idx;
+        const int i0 = id2 / M, j = id2 - i0 * M;
+        const int tau = blk16 ? 16 * i0 : i0;
         const float r = a.rho[k * M + j];
         const float th = a.theta[k * M + j];
         const float mag = tau == 0 ? 1.f : exp2f((float)tau * log2f(r));
         float sn, cs;
-        sincosf(th * (float)tau, &sn, &cs);   // |theta tau| <= 16 pi
+        sincosf(th * (float)tau, &sn, &cs);   // |theta tau| <= 64 pi
         const float pr = mag * cs, pi = mag * sn;
-        sm.pw[tau][j] = make_float2(pr, pi);
-        const float cr = a.c[(k * M + j) * 2], ci = a.c[(k * M + j) * 2 + 1];
-        sm.cpw[tau][j] = make_float2(cr * pr - ci * pi, cr * pi + ci * pr);
+        if (blk16) {
+            sm.p16[i0][j] = make_float2(pr, pi);
+        } else {
+            sm.pw[tau][j] = make_float2(pr, pi);
+            const float cr = a.c[(k * M + j) * 2], ci = a.c[(k * M + j) * 2 + 1];
+            sm.cpw[tau][j] = make_float2(cr * pr - ci * pi, cr * pi + ci * pr);
+        }
     }
     __syncthreads();
-    for (int tau = tid; tau < 16; tau += C::THREADS) {
+    // psi(16 d + r) = sum_j Re(c_j lambda_j^r lambda_j^{16 d})
+    for (int tau = tid; tau < C::BLK; tau += C::THREADS) {
+        const int d = tau >> 4, r = tau & 15;
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < M; ++j) s += sm.cpw[tau][j].x;
+        for (int j = 0; j < M; ++j) {
+            const float2 cp = sm.cpw[r][j], pd = sm.p16[d][j];
+            s += cp.x * pd.x - cp.y * pd.y;
+        }
         sm.psi[tau] = s;
     }
     __syncthreads();
 
     // ---- per-lane constant MFMA operands ------------------------------------------------
-    // by: B operand of the output product.  Lane (g, col) holds, for t = T0+col,
-    //   slots 0..3: psi(t-s) [s <= t] for s = T0+4g+e, and
-    //   slots 4..7: {Re, -Im}(c_j lambda_j^{t-T0+1}) for state rows 4g..4g+3.
-    // al: A operand of the state product.  Lane (g, col) holds, for state row
-    //   col = (j, re/im), {Re, Im}(lambda_j^{15-4g-e}) split into bf16 hi (slots
-    //   0..3) and lo (slots 4..7).
-    // l16: lambda_j^16 for this lane's modes 2g, 2g+1.
-    bf16x8_t by, al;
-    float l16[4];
+    // Output product of target sub-block a of a block (B operands; lane (g, col)
+    // is target position t = 16a + col of the block):
+    //   yD[a]: slots 0..3: psi(t-s) [s <= t] for s = 16a+4g+e (same for every a);
+    //          slots 4..7: {Re, -Im}(c_j lambda_j^{t+1}) for state rows 4g..4g+3.
+    //   yB12:  slots 0..3: psi(16+col-4g-e) (source sub-block a-1),
+    //          slots 4..7: psi(32+col-4g-e) (source sub-block a-2).
+    //   yB3:   slots 0..3: psi(48+col-4g-e) (source sub-block a-3), slots 4..7: 0.
+    // State product of source sub-block a (A operands; lane (g, col) is state
+    // row col = (j, re/im)): lpA[a]: {Re, Im}(lambda_j^{BLK-1-16a-4g-e}) split
+    // into bf16 hi (slots 0..3) and lo (slots 4..7).
+    // lB: lambda_j^BLK and l16: lambda_j^16 for this lane's modes 2g, 2g+1.
+    // The sub-block path uses yD[0] (its output operand) and lpA[NB-1] (its
+    // state operand).
+    constexpr int NB = C::NB, BLK = C::BLK;
+    bf16x8_t yD[NB], yB12, yB3, lpA[NB];
+    float lB[4], l16[4];
     {
         u16x8_t h;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int s = 4 * g + e;
-            h[e] = f32_to_bf16(s <= col ? sm.psi[col - s] : 0.f);
+        for (int aa = 0; aa < NB; ++aa) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 4 * g + e;
+                h[e] = f32_to_bf16(s <= col ? sm.psi[col - s] : 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i, j = row >> 1;
+                float val = 0.f;
+                if (j < M) {
+                    const float2 cp = sm.cpw[col + 1][j < M ? j : 0], pd = sm.p16[aa][j < M ? j : 0];
+                    val = (row & 1) ? -(cp.x * pd.y + cp.y * pd.x) : (cp.x * pd.x - cp.y * pd.y);
+                }
+                h[4 + i] = f32_to_bf16(val);
+            }
+            yD[aa] = to_bf16x8(h);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * g + i, j = row >> 1;
-            float val = 0.f;
-            if (j < M) {
-                const float2 cp = sm.cpw[col + 1][j < M ? j : 0];
-                val = (row & 1) ? -cp.y : cp.x;
-            }
-            h[4 + i] = f32_to_bf16(val);
+        for (int e = 0; e < 4; ++e) {
+            h[e] = NB >= 2 ? f32_to_bf16(sm.psi[(16 + col - 4 * g - e) & (BLK - 1)]) : 0;
+            h[4 + e] = NB >= 3 ? f32_to_bf16(sm.psi[(32 + col - 4 * g - e) & (BLK - 1)]) : 0;
         }
-        by = to_bf16x8(h);
+        yB12 = to_bf16x8(h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = NB >= 4 ? f32_to_bf16(sm.psi[(48 + col - 4 * g - e) & (BLK - 1)]) : 0;
+            h[4 + e] = 0;
+        }
+        yB3 = to_bf16x8(h);
         const int jr = col >> 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float val = 0.f;
-            if (jr < M) {
-                const float2 pw = sm.pw[15 - 4 * g - e][jr < M ? jr : 0];
-                val = (col & 1) ? pw.y : pw.x;
+        for (int aa = 0; aa < NB; ++aa) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float val = 0.f;
+                if (jr < M) {
+                    const float2 pw = sm.pw[15 - 4 * g - e][jr < M ? jr : 0];
+                    const float2 pd = sm.p16[NB - 1 - aa][jr < M ? jr : 0];
+                    val = (col & 1) ? (pw.x * pd.y + pw.y * pd.x) : (pw.x * pd.x - pw.y * pd.y);
+                }
+                const uint16_t hb = f32_to_bf16(val);
+                h[e] = hb;
+                h[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
             }
-            const uint16_t hb = f32_to_bf16(val);
-            h[e] = hb;
-            h[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
+            lpA[aa] = to_bf16x8(h);
         }
-        al = to_bf16x8(h);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * g + hh;
-            const float2 p16 = j < M ? sm.pw[16][j < M ? j : 0] : make_float2(0.f, 0.f);
-            l16[2 * hh] = p16.x;
-            l16[2 * hh + 1] = p16.y;
+            const float2 pb = j < M ? sm.p16[NB][j < M ? j : 0] : make_float2(0.f, 0.f);
+            const float2 p1 = j < M ? sm.p16[1][j < M ? j : 0] : make_float2(0.f, 0.f);
+            lB[2 * hh] = pb.x;
+            lB[2 * hh + 1] = pb.y;
+            l16[2 * hh] = p1.x;
+            l16[2 * hh + 1] = p1.y;
         }
     }
+    const bf16x8_t by = yD[0], al = lpA[NB - 1];
 
     // ---- state in the accumulator layout ---------------------------------------------
     // st_in: state entering position 0 (segment 0 only), read once up front so that
@@ -393,7 +453,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // Loads of one chunk held in registers until they are staged into LDS.
     struct ChunkRegs {
         uint4 v[C::NLD];
-        float cd[C::CPL], cw[C::CPL], cr[C::CPL];   // controls (wave 0 only)
+        float cd[C::CPL];                           // controls (wave 0 only); gates as
+        uint32_t cw[C::CPL], cr[C::CPL];            // raw bf16 bits, converted when staged
     };
 
     auto load_chunk = [&](ChunkRegs& rg, int c) {
@@ -416,12 +477,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 if (r < LC && t < L) {
                     const size_t row = ((size_t)b * L + t) * K + k;
                     rg.cd[u] = a.delta[row];
-                    rg.cw[u] = bf16_to_f32(gwg[row]);
-                    rg.cr[u] = bf16_to_f32(grg[row]);
+                    rg.cw[u] = gwg[row];
+                    rg.cr[u] = grg[row];
                 } else {
                     rg.cd[u] = 0.f;
-                    rg.cw[u] = 0.f;
-                    rg.cr[u] = 0.f;
+                    rg.cw[u] = 0u;
+                    rg.cr[u] = 0u;
                 }
             }
         }
@@ -429,8 +490,15 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 
     // Wave 0: clock sums and per-position factors of the staged chunk (n valid
     // positions) from the controls it holds.
-    auto stage_ctrl = [&](const float (&cd)[C::CPL], const float (&cw)[C::CPL], const float (&cr)[C::CPL], int n) {
+    auto stage_ctrl = [&](const float (&cd)[C::CPL], const uint32_t (&cwb)[C::CPL], const uint32_t (&crb)[C::CPL],
+                          int n) {
         if (wave == 0) {
+            float cw[C::CPL], cr[C::CPL];
+#pragma unroll
+            for (int u = 0; u < C::CPL; ++u) {
+                cw[u] = bf16_to_f32((uint16_t)cwb[u]);
+                cr[u] = bf16_to_f32((uint16_t)crb[u]);
+            }
             float loc[C::CPL];
             float run = 0.f;
 #pragma unroll
@@ -459,15 +527,31 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int u = 0; u < C::CPL; ++u) {
                 const int idx = lane * C::CPL + u;
                 if (idx < LC) {
-                    const int T0 = idx & ~15;
-                    const float qp = T0 > 0 ? sgp->q2[T0 - 1] : 0.f;
                     const float q = sgp->q2[idx];
-                    sgp->bq[idx] = idx < n ? exp2f(q - qp) * cw[u] : 0.f;
-                    sgp->ag[idx] = exp2f(qp - q) * cr[u];
-                    const int T1 = min(T0 + 15, n - 1);
-                    if (idx == T1) {
-                        const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
-                        sgp->blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
+                    // block of BLK positions: factored with the clock referenced to
+                    // its middle when it is whole and its span allows
+                    const int B0 = idx & ~(C::BLK - 1);
+                    const int B1 = min(B0 + C::BLK - 1, n - 1);
+                    const float qs = B0 > 0 ? sgp->q2[B0 - 1] : 0.f;
+                    const float qe = sgp->q2[B1 > 0 ? B1 : 0];
+                    if (B1 == B0 + C::BLK - 1 && qe - qs <= SPAN2_BLOCK_MAX) {
+                        const float ref = 0.5f * (qs + qe);
+                        sgp->bq[idx] = exp2f(q - ref) * cw[u];
+                        sgp->ag[idx] = exp2f(ref - q) * cr[u];
+                        if (idx == B1)
+                            sgp->blkB[B0 / C::BLK] = make_float4(exp2f(qs - ref), exp2f(ref - qe), exp2f(qs - qe), 0.f);
+                    } else {
+                        // sub-block factors (clock referenced to each sub-block's start)
+                        const int T0 = idx & ~15;
+                        const float qp = T0 > 0 ? sgp->q2[T0 - 1] : 0.f;
+                        sgp->bq[idx] = idx < n ? exp2f(q - qp) * cw[u] : 0.f;
+                        sgp->ag[idx] = exp2f(qp - q) * cr[u];
+                        const int T1 = min(T0 + 15, n - 1);
+                        if (idx == T1) {
+                            const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
+                            sgp->blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
+                        }
+                        if (idx == B1) sgp->blkB[B0 / C::BLK] = make_float4(0.f, 0.f, 0.f, 1.f);
                     }
                 }
             }
@@ -648,6 +732,94 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const float ar = tr[i], ai = tr[i + 1];
             tr[i] = ar * lam[i] - ai * lam[i + 1];
             tr[i + 1] = ar * lam[i + 1] + ai * lam[i];
+        }
+    };
+
+    // One whole block of NB sub-blocks with the clock referenced to its middle:
+    //   y(t) = a(t) g_r(t) [ sum_{s<=t} psi(t-s) b(s) v(s) + sum_j Re(c_j lambda_j^{t+1} H_s h_j) ]
+    //   h'   = Lambda_e lambda^BLK h + A_e sum_s lambda^{BLK-1-s} b(s) v(s)
+    // (positions relative to the block, H_s = a at the block's entry, A_e = a at
+    // its end, Lambda_e = e^{-clock span}).  The state is carried once per block;
+    // per sub-block only b(s) v(s) is formed (bf16 hi + lo) and fed to the
+    // constant-operand products.
+    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, float (&tr)[4]) {
+        const float4 bk = sgp->blkB[Bi];
+        uint2 hh[NTW];
+        if (out) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+                hh[nt] = make_uint2(pk_bf16(st[nt][0] * bk.x, st[nt][1] * bk.x),
+                                    pk_bf16(st[nt][2] * bk.x, st[nt][3] * bk.x));
+        }
+        f32x4_t mv[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) mv[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uint2 bvh[NB][NTW];
+        const uint2 z2 = make_uint2(0u, 0u);
+#pragma unroll
+        for (int aa = 0; aa < NB; ++aa) {
+            const int T = Bi * NB + aa, T0 = T * 16;
+            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const uint2 vfr = load_vfrag(T, nt);
+                const float x0 = b4.x * lo_f32(vfr.x), x1 = b4.y * hi_f32(vfr.x);
+                const float x2 = b4.z * lo_f32(vfr.y), x3 = b4.w * hi_f32(vfr.y);
+                const uint32_t h01 = pk_bf16(x0, x1), h23 = pk_bf16(x2, x3);
+                bvh[aa][nt] = make_uint2(h01, h23);
+                const uint2 bl = make_uint2(pk_bf16(x0 - lo_f32(h01), x1 - hi_f32(h01)),
+                                            pk_bf16(x2 - lo_f32(h23), x3 - hi_f32(h23)));
+                mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bvh[aa][nt], bvh[aa][nt]), mv[nt],
+                                                                 0, 0, 0);
+                mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bl, bl), mv[nt], 0, 0, 0);
+            }
+            if (out) {
+                const float sc = sgp->ag[T0 + col];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
+                                                                         f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if (aa >= 1)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2),
+                            yB12, acc, 0, 0, 0);
+                    if (aa >= 3)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa >= 3 ? aa - 3 : 0][nt], z2),
+                                                                     yB3, acc, 0, 0, 0);
+                    stage_y(T, nt, acc, sc);
+                }
+            }
+        }
+        float lam[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[i] = bk.z * lB[i];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float hr = st[nt][i], hi = st[nt][i + 1];
+                st[nt][i] = lam[i] * hr - lam[i + 1] * hi + bk.y * mv[nt][i];
+                st[nt][i + 1] = lam[i + 1] * hr + lam[i] * hi + bk.y * mv[nt][i + 1];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            const float ar = tr[i], ai = tr[i + 1];
+            tr[i] = ar * lam[i] - ai * lam[i + 1];
+            tr[i + 1] = ar * lam[i + 1] + ai * lam[i];
+        }
+    };
+
+    // All positions of the staged chunk (n valid): whole blocks on the block
+    // path, the others (ragged, or a clock span too large) sub-block by sub-block.
+    auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) {
+        for (int Bi = 0; Bi * BLK < n; ++Bi) {
+            if (sgp->blkB[Bi].w == 0.f) {
+                block_fast(st, Bi, out, tr);
+            } else {
+                const int tend = min(n, (Bi + 1) * BLK);
+                for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, out, tr);
+            }
         }
     };
 
@@ -848,7 +1020,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int i = 0; i < nck; ++i) {
                 const int n = min(LC, L - (c_begin + i) * LC);
                 sgp = &sm.stg[i];
-                for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, false, tr);
+                chunk_pass(st, n, false, tr);
             }
             between_sweeps();
         }
@@ -858,19 +1030,27 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const int t0 = (c_begin + i) * LC;
             const int n = min(LC, L - t0);
             sgp = &sm.stg[i];
-            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
+            chunk_pass(st, n, true, tr);
             store_y(t0, n);
         }
     } else {
-        // whole sequence, streamed through one staging buffer
+        // Whole sequence, streamed through one staging buffer.  The y of chunk
+        // c-1 stays staged until the loads of chunk c have been waited for, so
+        // that this wait never includes the stores of y (vector memory
+        // operations complete in issue order for the wait counter).
         load_chunk(rb, c_begin);
+        int yt0 = -1, yn = 0;
         for (int c = c_begin; c < c_end; ++c) {
             const int t0 = c * LC;
             const int n = min(LC, L - t0);
+            __builtin_amdgcn_s_waitcnt(WAIT_VMEM0);   // loads of chunk c, issued a chunk ago
+            if (yt0 >= 0) store_y(yt0, yn);          // each wave reads back only its own columns
             stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
-            for (int T = 0; T * 16 < n; ++T) subblock(st, T, n, true, tr);
-            store_y(t0, n);
+            chunk_pass(st, n, true, tr);
+            yt0 = t0;
+            yn = n;
         }
+        if (yt0 >= 0) store_y(yt0, yn);
     }
 
     // ---- leaving state ----------------------------------------------------------------------
