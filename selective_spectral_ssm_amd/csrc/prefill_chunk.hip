@@ -93,7 +93,7 @@ constexpr int WAIT_VMEM0 = 0x0F70;
 // Bytes of one staged chunk (v tile and per-position factors) and the number
 // of chunks a segment keeps resident in LDS (a budget of 40 KB per workgroup).
 constexpr int stage_bytes(int P, int LC) {
-    return LC * P * 2 + 5 * LC * 4 + (LC / 16) * 8 + (LC >= 64 ? LC / 64 : 1) * 16;
+    return LC * P * 2 + 5 * LC * 4 + (LC / 16) * 8 + (LC / 32) * 16;
 }
 constexpr int resident_chunks(int P, int LC) {
     return 40960 / stage_bytes(P, LC) < 1 ? 1 : (40960 / stage_bytes(P, LC) > 4 ? 4 : 40960 / stage_bytes(P, LC));
@@ -110,11 +110,10 @@ struct Cfg {
     static constexpr int THREADS = 64 * NW;
     static constexpr int WCOLS = 16 * NTW;          // value columns per wave
     static constexpr int NSB = LC / 16;             // 16-position sub-blocks per chunk
-    // Arithmetic blocks: NB sub-blocks (64 positions, or the whole chunk when
-    // it is shorter) whose state is carried once per block.
+    // Arithmetic blocks: NB sub-blocks whose state is carried once per block;
+    // at most 64 positions (the streamed path), 32 in the segmented path.
     static constexpr int NB = LC >= 64 ? 4 : LC / 16;
     static constexpr int BLK = 16 * NB;
-    static constexpr int NBLK = LC / BLK;           // blocks per chunk
     static constexpr int LPR = WCOLS / 8;           // lanes per v row (16 B each)
     static constexpr int RPI = 64 / LPR;            // v rows per wave load
     static constexpr int NLD = LC / RPI;            // wave loads per chunk
@@ -141,7 +140,7 @@ struct __align__(16) Stage {
     float bq[C::LC];                 // b(s) = e^{qh(s)-qh(T0-1)} g_w(s)   (0 beyond the chunk)
     float ag[C::LC];                 // a(t) g_r(t) = e^{-(qh(t)-qh(T0-1))} g_r(t)
     float2 blk[C::NSB];              // per sub-block: (A_T, 1 if the exact path is needed)
-    float4 blkB[C::NBLK];            // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed)
+    float4 blkB[C::LC / 32];         // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed)
     alignas(16) uint16_t V[C::LC * C::P];   // v tile [t][P] (swizzled units); y staged in place
 };
 
@@ -208,10 +207,15 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
 }
 
 template <class C, bool SEG>
-__global__ void __launch_bounds__(C::THREADS)
+// Segmented launches keep a workgroup's chunks resident in LDS (four
+// workgroups per CU); the register budget is held to match that occupancy.
+__global__ void __launch_bounds__(C::THREADS, SEG ? 4 : 1)
 prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr int LC = C::LC, M = C::M, P = C::P, WCOLS = C::WCOLS, NTW = C::NTW;
     constexpr int ROWS = 2 * M;          // state rows (mode, re/im) per value column
+    // sub-blocks per arithmetic block: fewer in the segmented path, where
+    // registers (four workgroups per CU) matter more than VALU work
+    constexpr int NB = SEG ? 2 : C::NB, BLK = 16 * NB;
     __shared__ Smem<C> sm;
 
     const int tid = threadIdx.x;
@@ -274,8 +278,10 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // tables below and, for the last segment, the look-back.
     // (gates kept as raw bf16 bits: converting them here would make the wave
     // wait for these loads, and so for every load issued before them)
-    float ecd[C::RES][C::CPL];
-    uint32_t ecw[C::RES][C::CPL], ecr[C::RES][C::CPL];
+    // Wave w holds the controls of resident chunks w, w + NW, ... and stages them.
+    constexpr int SPW = (C::RES + C::NW - 1) / C::NW;   // resident chunks per wave
+    float ecd[SPW][C::CPL];
+    uint32_t ecw[SPW][C::CPL], ecr[SPW][C::CPL];
     if (SEG) {
         constexpr int UPR = P / 8;                 // 16-byte units per tile row
         constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
@@ -291,20 +297,21 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
                     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&sm.stg[i].V[ins * 512]), 16, 0, 0);
                 }
-                if (wave == 0) {
+                if (wave == i % C::NW) {
+                    const int q = i / C::NW;
 #pragma unroll
                     for (int u = 0; u < C::CPL; ++u) {
                         const int rr = lane * C::CPL + u;
                         const int t = (c_begin + i) * LC + rr;
                         if (rr < LC && t < L) {
                             const size_t row = ((size_t)b * L + t) * K + k;
-                            ecd[i][u] = a.delta[row];
-                            ecw[i][u] = gwg[row];
-                            ecr[i][u] = grg[row];
+                            ecd[q][u] = a.delta[row];
+                            ecw[q][u] = gwg[row];
+                            ecr[q][u] = grg[row];
                         } else {
-                            ecd[i][u] = 0.f;
-                            ecw[i][u] = 0u;
-                            ecr[i][u] = 0u;
+                            ecd[q][u] = 0.f;
+                            ecw[q][u] = 0u;
+                            ecr[q][u] = 0u;
                         }
                     }
                 }
@@ -360,7 +367,6 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // lB: lambda_j^BLK and l16: lambda_j^16 for this lane's modes 2g, 2g+1.
     // The sub-block path uses yD[0] (its output operand) and lpA[NB-1] (its
     // state operand).
-    constexpr int NB = C::NB, BLK = C::BLK;
     bf16x8_t yD[NB], yB12, yB3, lpA[NB];
     float lB[4], l16[4];
     {
@@ -488,11 +494,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     };
 
-    // Wave 0: clock sums and per-position factors of the staged chunk (n valid
-    // positions) from the controls it holds.
+    // One wave: clock sums and per-position factors of the staged chunk (n
+    // valid positions) from the controls it holds.
     auto stage_ctrl = [&](const float (&cd)[C::CPL], const uint32_t (&cwb)[C::CPL], const uint32_t (&crb)[C::CPL],
                           int n) {
-        if (wave == 0) {
+        {
             float cw[C::CPL], cr[C::CPL];
 #pragma unroll
             for (int u = 0; u < C::CPL; ++u) {
@@ -530,16 +536,16 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     const float q = sgp->q2[idx];
                     // block of BLK positions: factored with the clock referenced to
                     // its middle when it is whole and its span allows
-                    const int B0 = idx & ~(C::BLK - 1);
-                    const int B1 = min(B0 + C::BLK - 1, n - 1);
+                    const int B0 = idx & ~(BLK - 1);
+                    const int B1 = min(B0 + BLK - 1, n - 1);
                     const float qs = B0 > 0 ? sgp->q2[B0 - 1] : 0.f;
                     const float qe = sgp->q2[B1 > 0 ? B1 : 0];
-                    if (B1 == B0 + C::BLK - 1 && qe - qs <= SPAN2_BLOCK_MAX) {
+                    if (B1 == B0 + BLK - 1 && qe - qs <= SPAN2_BLOCK_MAX) {
                         const float ref = 0.5f * (qs + qe);
                         sgp->bq[idx] = exp2f(q - ref) * cw[u];
                         sgp->ag[idx] = exp2f(ref - q) * cr[u];
                         if (idx == B1)
-                            sgp->blkB[B0 / C::BLK] = make_float4(exp2f(qs - ref), exp2f(ref - qe), exp2f(qs - qe), 0.f);
+                            sgp->blkB[B0 / BLK] = make_float4(exp2f(qs - ref), exp2f(ref - qe), exp2f(qs - qe), 0.f);
                     } else {
                         // sub-block factors (clock referenced to each sub-block's start)
                         const int T0 = idx & ~15;
@@ -551,7 +557,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
                             sgp->blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
                         }
-                        if (idx == B1) sgp->blkB[B0 / C::BLK] = make_float4(0.f, 0.f, 0.f, 1.f);
+                        if (idx == B1) sgp->blkB[B0 / BLK] = make_float4(0.f, 0.f, 0.f, 1.f);
                     }
                 }
             }
@@ -568,7 +574,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const int tr = i * C::RPI + vrow_l;
             *reinterpret_cast<uint4*>(&sgp->V[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
         }
-        stage_ctrl(rg.cd, rg.cw, rg.cr, n);
+        if (wave == 0) stage_ctrl(rg.cd, rg.cw, rg.cr, n);
         if (next >= 0) load_chunk(rg, next);
         __syncthreads();
     };
@@ -1009,10 +1015,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         wait_stores_complete();   // this wave's tile loads have landed
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < C::RES; ++i) {
+        for (int q = 0; q < SPW; ++q) {
+            const int i = q * C::NW + wave;
             if (i < nck) {
                 sgp = &sm.stg[i];
-                stage_ctrl(ecd[i], ecw[i], ecr[i], min(LC, L - (c_begin + i) * LC));
+                stage_ctrl(ecd[q], ecw[q], ecr[q], min(LC, L - (c_begin + i) * LC));
             }
         }
         __syncthreads();
