@@ -209,7 +209,7 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
 template <class C, bool SEG>
 // Segmented launches keep a workgroup's chunks resident in LDS (four
 // workgroups per CU); the register budget is held to match that occupancy.
-__global__ void __launch_bounds__(C::THREADS, SEG ? 4 : 1)
+__global__ void __launch_bounds__(C::THREADS, SEG && C::NW == 4 ? 4 : 1)
 prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr int LC = C::LC, M = C::M, P = C::P, WCOLS = C::WCOLS, NTW = C::NTW;
     constexpr int ROWS = 2 * M;          // state rows (mode, re/im) per value column
