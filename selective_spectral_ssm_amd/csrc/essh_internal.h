@@ -93,7 +93,17 @@ enum {
 };
 enum : unsigned { SCAN_ERR_TIMEOUT = 1u, SCAN_ERR_TICKET = 2u };
 
+// How a chunked prefill launch covers the sequences (one per batch row and
+// retained channel):
+//   SCAN_WHOLE     one workgroup streams a whole sequence;
+//   SCAN_LOOKBACK  segments of a sequence in one launch, each obtaining its
+//                  entering state by a decoupled look-back over its predecessors;
+//   SCAN_SPLIT     three launches: segment aggregates, a scan over segments,
+//                  then every segment streamed from its entering state.
+enum { SCAN_WHOLE = 0, SCAN_LOOKBACK = 1, SCAN_SPLIT = 2 };
+
 struct ScanPlan {
+    int mode;
     int nseq, nchunks, seg_chunks, nseg, nblocks;
     unsigned* hdr;
     unsigned* flags;

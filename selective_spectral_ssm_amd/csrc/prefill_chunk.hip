@@ -41,8 +41,14 @@
 // Lambda_seg), (ii) publishes it, (iii) obtains its entering state by a
 // decoupled look-back over its predecessors' published aggregates / inclusive
 // states, publishes its own inclusive state, and (iv) sweeps the segment
-// again with the true entering state, now producing y.  The second sweep
-// re-reads v, which the first sweep has just brought into the caches.
+// again with the true entering state, now producing y.  The segment's chunks
+// stay resident in LDS between the two sweeps, so v is read once.
+//
+// Three-launch scan.  With very few sequences the look-back chains get long;
+// then (i) one launch computes every segment's aggregate (end state from a
+// zero entering state, or from state_in for segment 0) and transfer, (ii) a
+// small scan composes them per sequence into entering states, and (iii) every
+// segment is streamed from its entering state producing y.  v is read twice.
 //
 // gfx950 mapping
 //   * Each wave owns 16*NTW value columns for all positions: its share of the
@@ -146,7 +152,6 @@ struct __align__(16) Stage {
 
 template <class C>
 struct __align__(16) Smem {
-    Stage<C> stg[C::RES];
     float2 pw[17][C::M];             // lambda_j^tau, tau = 0..16
     float2 cpw[17][C::M];            // c_j lambda_j^tau
     float2 p16[C::NB + 1][C::M];     // lambda_j^{16 d}, d = 0..NB
@@ -206,17 +211,27 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
     return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
 }
 
-template <class C, bool SEG>
+// Kernel roles (template argument MODE): a whole sequence or a segment streamed
+// from its entering state (STREAM), a segment of a look-back scan (LOOKBACK),
+// or the end state of a segment from a zero entering state (AGG).
+enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2 };
+
+template <class C, int MODE>
 // Segmented launches keep a workgroup's chunks resident in LDS (four
 // workgroups per CU); the register budget is held to match that occupancy.
-__global__ void __launch_bounds__(C::THREADS, SEG && C::NW == 4 ? 4 : 1)
+__global__ void __launch_bounds__(C::THREADS, MODE == MODE_LOOKBACK && C::NW == 4 ? 4 : 1)
 prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr int LC = C::LC, M = C::M, P = C::P, WCOLS = C::WCOLS, NTW = C::NTW;
     constexpr int ROWS = 2 * M;          // state rows (mode, re/im) per value column
+    constexpr bool SEG = MODE == MODE_LOOKBACK;
+    constexpr bool AGG = MODE == MODE_AGG;
     // sub-blocks per arithmetic block: fewer in the segmented path, where
     // registers (four workgroups per CU) matter more than VALU work
     constexpr int NB = SEG ? 2 : C::NB, BLK = 16 * NB;
+    // The staged chunks are an LDS object of their own, so that accesses to
+    // the tables in sm are not ordered behind the asynchronous tile copies.
     __shared__ Smem<C> sm;
+    __shared__ Stage<C> stg[MODE == MODE_LOOKBACK ? C::RES : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -236,10 +251,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         // the work items x, x + 8, x + 16, ... in start order.
         const int xq = (int)(blockIdx.x & 7u);
         if (tid == 0) {
+            const unsigned ep = ld_agent_u(&plan.hdr[SCAN_HDR_EPOCH]);
             const unsigned t = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_TICKET0 + SCAN_HDR_STRIDE * xq], 1u,
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sm.ticket = (int)(t * 8u + (unsigned)xq);
-            sm.epoch = ld_agent_u(&plan.hdr[SCAN_HDR_EPOCH]);
+            sm.epoch = ep;
         }
         __syncthreads();
         const int ticket = sm.ticket;
@@ -253,8 +269,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         seg = ticket / plan.nseq;
         seq = ticket - seg * plan.nseq;
     } else {
-        seq = remap_xcd(blockIdx.x, gridDim.x);
-        seg = 0;
+        // segment-major order: neighbouring work items are neighbouring channels
+        // of one batch row over the same positions
+        const int item = remap_xcd(blockIdx.x, gridDim.x);
+        seg = item / plan.nseq;
+        seq = item - seg * plan.nseq;
     }
     const int k = seq % a.K_T;
     const int b = seq / a.K_T;
@@ -271,56 +290,62 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     uint16_t* yg = static_cast<uint16_t*>(a.y);
 
     // ---- segmented scan: every chunk of the segment is requested at once -------------------
-    // v tiles go straight into their LDS stage buffers (global_load_lds, 16
-    // bytes per lane; a wave instruction fills 1 KB of the tile, so each lane
-    // fetches the 16-byte unit whose swizzled slot is lane-th of that block),
-    // the controls into wave 0's registers.  These loads overlap the pole
-    // tables below and, for the last segment, the look-back.
-    // (gates kept as raw bf16 bits: converting them here would make the wave
-    // wait for these loads, and so for every load issued before them)
-    // Wave w holds the controls of resident chunks w, w + NW, ... and stages them.
+    // The controls (wave w holds those of resident chunks w, w + NW, ...; the
+    // gates as raw bf16 bits), then the v tiles straight into their LDS stage
+    // buffers (global_load_lds, 16 bytes per lane; a wave instruction fills 1
+    // KB of the tile, so each lane fetches the 16-byte unit whose swizzled
+    // slot is lane-th of that block).
     constexpr int SPW = (C::RES + C::NW - 1) / C::NW;   // resident chunks per wave
     float ecd[SPW][C::CPL];
     uint32_t ecw[SPW][C::CPL], ecr[SPW][C::CPL];
+    const int nck = c_end - c_begin;
     if (SEG) {
-        constexpr int UPR = P / 8;                 // 16-byte units per tile row
-        constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
-        const int nck = c_end - c_begin;
 #pragma unroll
-        for (int i = 0; i < C::RES; ++i) {
+        for (int q = 0; q < SPW; ++q) {
+            const int i = q * C::NW + wave;
             if (i < nck) {
-                for (int ins = wave; ins < INSTR; ins += C::NW) {
-                    const int sl = ins * 64 + lane;
-                    const int r = sl / UPR, pu = sl - r * UPR;
-                    const int u = pu ^ (((r / C::RP256) & C::SWZ_MASK) << 1);
-                    const int t = min((c_begin + i) * LC + r, L - 1);   // rows past L: any valid row
-                    const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
-                    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&sm.stg[i].V[ins * 512]), 16, 0, 0);
-                }
-                if (wave == i % C::NW) {
-                    const int q = i / C::NW;
 #pragma unroll
-                    for (int u = 0; u < C::CPL; ++u) {
-                        const int rr = lane * C::CPL + u;
-                        const int t = (c_begin + i) * LC + rr;
-                        if (rr < LC && t < L) {
-                            const size_t row = ((size_t)b * L + t) * K + k;
-                            ecd[q][u] = a.delta[row];
-                            ecw[q][u] = gwg[row];
-                            ecr[q][u] = grg[row];
-                        } else {
-                            ecd[q][u] = 0.f;
-                            ecw[q][u] = 0u;
-                            ecr[q][u] = 0u;
-                        }
+                for (int u = 0; u < C::CPL; ++u) {
+                    const int rr = lane * C::CPL + u;
+                    const int t = (c_begin + i) * LC + rr;
+                    if (rr < LC && t < L) {
+                        const size_t row = ((size_t)b * L + t) * K + k;
+                        ecd[q][u] = a.delta[row];
+                        ecw[q][u] = gwg[row];
+                        ecr[q][u] = grg[row];
+                    } else {
+                        ecd[q][u] = 0.f;
+                        ecw[q][u] = 0u;
+                        ecr[q][u] = 0u;
                     }
                 }
             }
         }
     }
+    constexpr int NPOLE = (18 + C::NB) * M;
+    if (SEG) {
+        constexpr int UPR = P / 8;                 // 16-byte units per tile row
+        constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
+        static_assert(INSTR % C::NW == 0, "tile instructions must divide over the waves");
+        // all RES stages are requested (rows past the segment's last chunk
+        // repeat a valid row), so the count of these loads is fixed
+#pragma unroll
+        for (int i = 0; i < C::RES; ++i) {
+#pragma unroll
+            for (int it = 0; it < INSTR / C::NW; ++it) {
+                const int ins = it * C::NW + wave;
+                const int sl = ins * 64 + lane;
+                const int r = sl / UPR, pu = sl - r * UPR;
+                const int u = pu ^ (((r / C::RP256) & C::SWZ_MASK) << 1);
+                const int t = min((c_begin + i) * LC + r, L - 1);   // rows past L: any valid row
+                const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&stg[i].V[ins * 512]), 16, 0, 0);
+            }
+        }
+    }
 
     // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16, lambda^{16 d} ---------
-    for (int idx = tid; idx < (18 + C::NB) * M; idx += C::THREADS) {
+    for (int idx = tid; idx < NPOLE; idx += C::THREADS) {
         const bool blk16 = idx >= 17 * M;
         const int id2 = blk16 ? idx - 17 * M : idx;
         const int i0 = id2 / M, j = id2 - i0 * M;
@@ -433,8 +458,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const bf16x8_t by = yD[0], al = lpA[NB - 1];
 
     // ---- state in the accumulator layout ---------------------------------------------
-    // st_in: state entering position 0 (segment 0 only), read once up front so that
-    // an aliasing state_out written by the last segment cannot race with it.
+    // st_in: the entering state.  Segment 0 of a whole-sequence or look-back
+    // launch reads state_in once up front, so that an aliasing state_out
+    // written by the last segment cannot race with it.  In the three-launch
+    // scan the aggregate launch copies state_in into the entering-state slot
+    // of segment 0 and the streaming launch reads only those slots.
+    const bool split_stream = MODE == MODE_STREAM && nseg > 1;
     f32x4_t st_in[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
@@ -443,7 +472,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         for (int i = 0; i < 4; ++i) {
             const int row = 4 * g + i, j = row >> 1, cmp = row & 1;
             float x = 0.f;
-            if (seg == 0 && a.state_in && j < M) x = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
+            if (split_stream) {
+                if (row < ROWS) x = plan.incl[((slot + seg) * ROWS + row) * (size_t)P + p];
+            } else if (seg == 0 && a.state_in && j < M) {
+                x = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
+            }
             st_in[nt][i] = x;
         }
     }
@@ -452,7 +485,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const int vrow_l = lane / C::LPR;          // row of this lane inside a wave load
     const int vunit = lane % C::LPR;           // 16-byte unit of this lane inside a row
     const size_t vcol0 = (size_t)wave * WCOLS + vunit * 8;
-    Stage<C>* sgp = &sm.stg[0];   // staged chunk the helpers work on
+    Stage<C>* sgp = &stg[0];   // staged chunk the helpers work on
     // element offset of (row r, first column of 16-byte unit u) in the v tile
     auto vt_off = [&](int r, int u) { return r * P + ((u ^ (((r / C::RP256) & C::SWZ_MASK) << 1)) << 3); };
 
@@ -1004,7 +1037,6 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     ChunkRegs rb;
     if (SEG) {
         // Segment: its (at most RES) chunks were requested up front and stay in LDS.
-        const int nck = c_end - c_begin;
         if (!has_succ && seg > 0) {
             // last segment: only the entering state is needed
             f32x4_t e[NTW];
@@ -1018,7 +1050,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         for (int q = 0; q < SPW; ++q) {
             const int i = q * C::NW + wave;
             if (i < nck) {
-                sgp = &sm.stg[i];
+                sgp = &stg[i];
                 stage_ctrl(ecd[q], ecw[q], ecr[q], min(LC, L - (c_begin + i) * LC));
             }
         }
@@ -1026,7 +1058,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         if (has_succ) {
             for (int i = 0; i < nck; ++i) {
                 const int n = min(LC, L - (c_begin + i) * LC);
-                sgp = &sm.stg[i];
+                sgp = &stg[i];
                 chunk_pass(st, n, false, tr);
             }
             between_sweeps();
@@ -1036,32 +1068,57 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         for (int i = 0; i < nck; ++i) {
             const int t0 = (c_begin + i) * LC;
             const int n = min(LC, L - t0);
-            sgp = &sm.stg[i];
+            sgp = &stg[i];
             chunk_pass(st, n, true, tr);
             store_y(t0, n);
         }
     } else {
-        // Whole sequence, streamed through one staging buffer.  The y of chunk
-        // c-1 stays staged until the loads of chunk c have been waited for, so
-        // that this wait never includes the stores of y (vector memory
-        // operations complete in issue order for the wait counter).
+        // Whole sequence or segment, streamed through one staging buffer.  The
+        // y of chunk c-1 stays staged until the loads of chunk c have been
+        // waited for, so that this wait never includes the stores of y (vector
+        // memory operations complete in issue order for the wait counter).
         load_chunk(rb, c_begin);
         int yt0 = -1, yn = 0;
         for (int c = c_begin; c < c_end; ++c) {
             const int t0 = c * LC;
             const int n = min(LC, L - t0);
             __builtin_amdgcn_s_waitcnt(WAIT_VMEM0);   // loads of chunk c, issued a chunk ago
-            if (yt0 >= 0) store_y(yt0, yn);          // each wave reads back only its own columns
+            if (!AGG && yt0 >= 0) store_y(yt0, yn);  // each wave reads back only its own columns
             stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
-            chunk_pass(st, n, true, tr);
+            chunk_pass(st, n, !AGG, tr);
             yt0 = t0;
             yn = n;
         }
-        if (yt0 >= 0) store_y(yt0, yn);
+        if (!AGG && yt0 >= 0) store_y(yt0, yn);
+    }
+
+    // ---- segment aggregate (three-launch scan) ----------------------------------------------
+    if (AGG) {
+        float* dst = plan.agg + (slot + seg) * (size_t)ROWS * P;
+        float* ent = plan.incl + slot * (size_t)ROWS * P;   // entering state of segment 0
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = wave * WCOLS + nt * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                if (row < ROWS) {
+                    dst[(size_t)row * P + p] = st[nt][i];
+                    if (seg == 0) ent[(size_t)row * P + p] = st_in[nt][i];
+                }
+            }
+        }
+        if (wave == 0 && col == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                if (row < ROWS) plan.lam[(slot + seg) * ROWS + row] = tr[i];
+            }
+        }
     }
 
     // ---- leaving state ----------------------------------------------------------------------
-    if (seg + 1 >= nseg && a.state_out) {
+    if (!AGG && seg + 1 >= nseg && a.state_out) {
         const size_t base = ((size_t)b * K + k) * M;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -1100,16 +1157,91 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     }
 }
 
+// Aggregates per workgroup of the segment scan.
+constexpr int SCAN_PER = 16;
+
+// Entering states of the segments of every sequence from the segment
+// aggregates: E_1 = S_0 (segment 0's aggregate starts from state_in) and
+// E_{s+1} = Lambda_s E_s + S_s, the composition of Eq. 6's affine maps.  One
+// workgroup per (sequence, mode); thread (p, grp) composes the aggregates of
+// segments [16 grp, 16 grp + 16) for value column p, the groups' compositions
+// are exchanged through LDS, and each group then writes its entering states.
+__global__ void __launch_bounds__(1024) seg_scan_kernel(ScanPlan plan, int m, int P) {
+    __shared__ float4 comp[1024];
+    const int ROWS = 2 * m;
+    const int seq = blockIdx.x / m, j = blockIdx.x - seq * m;
+    const int p = threadIdx.x % P, grp = threadIdx.x / P;
+    const int nag = plan.nseg - 1;
+    const int s0 = grp * SCAN_PER;
+    const size_t slot = (size_t)seq * plan.nseg;
+    float lr[SCAN_PER], li[SCAN_PER], sr[SCAN_PER], si[SCAN_PER];
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) {
+        const int sg = s0 + i;
+        if (sg < nag) {
+            lr[i] = plan.lam[(slot + sg) * ROWS + 2 * j];
+            li[i] = plan.lam[(slot + sg) * ROWS + 2 * j + 1];
+            sr[i] = plan.agg[((slot + sg) * ROWS + 2 * j) * (size_t)P + p];
+            si[i] = plan.agg[((slot + sg) * ROWS + 2 * j + 1) * (size_t)P + p];
+        } else {
+            lr[i] = 1.f;
+            li[i] = 0.f;
+            sr[i] = 0.f;
+            si[i] = 0.f;
+        }
+    }
+    // composition of this group's maps: x -> A x + Bv
+    float ar = 1.f, ai = 0.f, br = 0.f, bi = 0.f;
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) {
+        const float nar = lr[i] * ar - li[i] * ai, nai = lr[i] * ai + li[i] * ar;
+        const float nbr = lr[i] * br - li[i] * bi + sr[i], nbi = lr[i] * bi + li[i] * br + si[i];
+        ar = nar;
+        ai = nai;
+        br = nbr;
+        bi = nbi;
+    }
+    comp[threadIdx.x] = make_float4(ar, ai, br, bi);
+    __syncthreads();
+    float hr = 0.f, hi = 0.f;   // value entering this group's first segment map
+    for (int q = 0; q < grp; ++q) {
+        const float4 f = comp[q * P + p];
+        const float nr = f.x * hr - f.y * hi + f.z, ni = f.x * hi + f.y * hr + f.w;
+        hr = nr;
+        hi = ni;
+    }
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) {
+        const int sg = s0 + i;
+        if (sg < nag) {
+            const float nr = lr[i] * hr - li[i] * hi + sr[i], ni = lr[i] * hi + li[i] * hr + si[i];
+            hr = nr;
+            hi = ni;
+            plan.incl[((slot + sg + 1) * ROWS + 2 * j) * (size_t)P + p] = hr;
+            plan.incl[((slot + sg + 1) * ROWS + 2 * j + 1) * (size_t)P + p] = hi;
+        }
+    }
+}
+
 template <int P, int M, int LC>
 hipError_t launch_cfg(const PrefillArgs& a, const ScanPlan& plan, hipStream_t s) {
     using C = Cfg<P, M, LC>;
     if (plan.nblocks == 0) return hipSuccess;
-    if (plan.nseg > 1)
-        hipLaunchKernelGGL((prefill_chunk_kernel<C, true>), dim3((unsigned)plan.nblocks), dim3(C::THREADS), 0, s, a,
+    if (plan.mode == SCAN_LOOKBACK) {
+        hipLaunchKernelGGL((prefill_chunk_kernel<C, MODE_LOOKBACK>), dim3((unsigned)plan.nblocks), dim3(C::THREADS),
+                           0, s, a, plan);
+        return hipGetLastError();
+    }
+    if (plan.mode == SCAN_SPLIT && plan.nseg > 1) {
+        const int nagg = plan.nseq * (plan.nseg - 1);   // every segment but the last
+        hipLaunchKernelGGL((prefill_chunk_kernel<C, MODE_AGG>), dim3((unsigned)nagg), dim3(C::THREADS), 0, s, a,
                            plan);
-    else
-        hipLaunchKernelGGL((prefill_chunk_kernel<C, false>), dim3((unsigned)plan.nblocks), dim3(C::THREADS), 0, s, a,
-                           plan);
+        const int ngrp = (plan.nseg - 1 + SCAN_PER - 1) / SCAN_PER;
+        hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(plan.nseq * M)), dim3((unsigned)(P * ngrp)), 0, s, plan,
+                           M, P);
+    }
+    hipLaunchKernelGGL((prefill_chunk_kernel<C, MODE_STREAM>), dim3((unsigned)plan.nblocks), dim3(C::THREADS), 0, s,
+                       a, plan);
     return hipGetLastError();
 }
 
@@ -1152,14 +1284,35 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc) {
     if (p.nseq == 0 || p.nchunks == 0) return p;
     // With about 1.5 sequences per CU or more, whole sequences keep the GPU
     // busy.  Below that, sequences are cut into segments of as many chunks as
-    // a workgroup keeps resident in LDS, so that v is read from memory once.
+    // a workgroup keeps resident in LDS, and a look-back scan links them.
+    // With very few sequences a round of resident workgroups (about 1000)
+    // covers many segments of each sequence, so each look-back would fold
+    // dozens of predecessors; there the three-launch scan is used instead,
+    // with about SPLIT_TARGET segments overall (at most what one scan
+    // workgroup composes per sequence).
     constexpr int SEQ_ENOUGH = 384;
+    constexpr int SPLIT_MAX_SEQ = 32;
+    constexpr int SPLIT_TARGET = 1536;
     int seg_chunks = p.nchunks;
-    if (p.nseq < SEQ_ENOUGH) seg_chunks = resident_chunks(P, Lc);
+    p.mode = SCAN_WHOLE;
+    if (p.nseq < SEQ_ENOUGH) {
+        if (p.nseq <= SPLIT_MAX_SEQ) {
+            p.mode = SCAN_SPLIT;
+            const long long want = ((long long)p.nchunks * p.nseq + SPLIT_TARGET - 1) / SPLIT_TARGET;
+            const int max_seg = 1 + SCAN_PER * (1024 / P);
+            const int min_chunks = (p.nchunks + max_seg - 1) / max_seg;
+            seg_chunks = (int)(want > min_chunks ? want : min_chunks);
+        } else {
+            p.mode = SCAN_LOOKBACK;
+            seg_chunks = resident_chunks(P, Lc);
+        }
+    }
+    if (seg_chunks < 1) seg_chunks = 1;
     if (seg_chunks > p.nchunks) seg_chunks = p.nchunks;
     p.seg_chunks = seg_chunks;
     p.nseg = (p.nchunks + seg_chunks - 1) / seg_chunks;
     p.nblocks = p.nseq * p.nseg;
+    if (p.nseg == 1) p.mode = SCAN_WHOLE;
     (void)m;
     return p;
 }
