@@ -111,6 +111,27 @@ def copy_bandwidth(mib=1024, reps=10):
     return 2 * n * 4 / sec / 1e9
 
 
+def copy_time_us(total_bytes, reps=50):
+    """Mean time of a plain elementwise copy that reads total_bytes/2 and writes
+    total_bytes/2: what moving a kernel's bytes costs at this size, launch
+    ramp-up and drain included."""
+    import torch
+    n = max(1, total_bytes // 8)
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SLEEP_CYCLES // 4)
+    for a, b in evs:
+        a.record()
+        torch.neg(src, out=dst)
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
+
+
 def time_launches(fn, steps, warmup):
     """Returns (ms per step over the whole timed region, mean ms per launch from per-launch events)."""
     import torch
@@ -223,7 +244,7 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
         times.append((time.perf_counter() - t0) * 1e6 / n_steps)
     nbytes = sizes.decode_bytes(NL, 1, K_T, w.m, w.P, "bf16")
     kmean = statistics.mean(per)
-    return dict(workload=w.name, layers=NL, K_T=K_T, steps=n_steps,
+    return dict(workload=w.name, layers=NL, K_T=K_T, steps=n_steps, copy_same_bytes_us=copy_time_us(nbytes),
                 us_per_step_graph=statistics.median(times), us_per_step_graph_all=times,
                 us_per_kernel_mean=kmean, us_per_kernel_median=statistics.median(per),
                 alg_bytes_per_step=nbytes, achieved_GBs=nbytes / (kmean * 1e-6) / 1e9,
@@ -307,6 +328,7 @@ def main():
                      "traffic_bytes_per_launch": traffic,
                      "alg_bytes_per_launch": main_res["alg_bytes"],
                      "copy_GBs": copy_gbs, "frac_of_copy": main_res["achieved_GBs"] / copy_gbs,
+                     "copy_same_bytes_us": copy_time_us(main_res["alg_bytes"]),
                      "us_per_launch": main_res["us_per_launch"]},
     }
     if not args.no_decode:
