@@ -146,7 +146,8 @@ struct __align__(16) Stage {
     float bq[C::LC];                 // b(s) = e^{qh(s)-qh(T0-1)} g_w(s)   (0 beyond the chunk)
     float ag[C::LC];                 // a(t) g_r(t) = e^{-(qh(t)-qh(T0-1))} g_r(t)
     float2 blk[C::NSB];              // per sub-block: (A_T, 1 if the exact path is needed)
-    float4 blkB[C::LC / 32];         // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed)
+    float4 blkB[C::LC / 32];         // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed);
+                                     // Lambda_e = e^{-clock span} also on the sub-block path
     alignas(16) uint16_t V[C::LC * C::P];   // v tile [t][P] (swizzled units); y staged in place
 };
 
@@ -225,9 +226,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr int ROWS = 2 * M;          // state rows (mode, re/im) per value column
     constexpr bool SEG = MODE == MODE_LOOKBACK;
     constexpr bool AGG = MODE == MODE_AGG;
-    // sub-blocks per arithmetic block: fewer in the segmented path, where
-    // registers (four workgroups per CU) matter more than VALU work
-    constexpr int NB = SEG ? 2 : C::NB, BLK = 16 * NB;
+    constexpr int NB = C::NB, BLK = C::BLK;   // sub-blocks per arithmetic block
     // The staged chunks are an LDS object of their own, so that accesses to
     // the tables in sm are not ordered behind the asynchronous tile copies.
     __shared__ Smem<C> sm;
@@ -392,9 +391,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // lB: lambda_j^BLK and l16: lambda_j^16 for this lane's modes 2g, 2g+1.
     // The sub-block path uses yD[0] (its output operand) and lpA[NB-1] (its
     // state operand).
+    // The output operands (yD, yB12, yB3) and the state operands (lpA, lB, l16)
+    // are built separately: the look-back launch needs the state operands in
+    // its aggregate sweep and the output operands in its output sweep only.
     bf16x8_t yD[NB], yB12, yB3, lpA[NB];
     float lB[4], l16[4];
-    {
+    auto make_out_constants = [&]() {
         u16x8_t h;
 #pragma unroll
         for (int aa = 0; aa < NB; ++aa) {
@@ -427,6 +429,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             h[4 + e] = 0;
         }
         yB3 = to_bf16x8(h);
+    };
+    auto make_state_constants = [&]() {
+        u16x8_t h;
         const int jr = col >> 1;
 #pragma unroll
         for (int aa = 0; aa < NB; ++aa) {
@@ -454,8 +459,36 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             l16[2 * hh] = p1.x;
             l16[2 * hh + 1] = p1.y;
         }
-    }
-    const bf16x8_t by = yD[0], al = lpA[NB - 1];
+    };
+    // The sub-block path's state operand (lpA[NB-1]) and lambda^16, rebuilt
+    // from the tables where the state operands are no longer held.
+    auto make_sub_al = [&]() -> bf16x8_t {
+        u16x8_t h;
+        const int jr = col >> 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float val = 0.f;
+            if (jr < M) {
+                const float2 pw = sm.pw[15 - 4 * g - e][jr < M ? jr : 0];
+                val = (col & 1) ? pw.y : pw.x;
+            }
+            const uint16_t hb = f32_to_bf16(val);
+            h[e] = hb;
+            h[4 + e] = f32_to_bf16(val - bf16_to_f32(hb));
+        }
+        return to_bf16x8(h);
+    };
+    auto make_l16 = [&](float (&o)[4]) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int j = 2 * g + hh;
+            const float2 p1 = j < M ? sm.p16[1][j < M ? j : 0] : make_float2(0.f, 0.f);
+            o[2 * hh] = p1.x;
+            o[2 * hh + 1] = p1.y;
+        }
+    };
+    make_state_constants();
+    if (!SEG) make_out_constants();
 
     // ---- state in the accumulator layout ---------------------------------------------
     // st_in: the entering state.  Segment 0 of a whole-sequence or look-back
@@ -590,7 +623,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             const bool exact = (q - qp) > SPAN2_FAST_MAX || T1 - T0 < 15;
                             sgp->blk[idx >> 4] = make_float2(exp2f(qp - q), exact ? 1.f : 0.f);
                         }
-                        if (idx == B1) sgp->blkB[B0 / BLK] = make_float4(0.f, 0.f, 0.f, 1.f);
+                        if (idx == B1) sgp->blkB[B0 / BLK] = make_float4(0.f, 0.f, exp2f(qs - qe), 1.f);
                     }
                 }
             }
@@ -644,7 +677,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
-    auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4]) {
+    auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4], const bf16x8_t& al,
+                        const float (&l16)[4]) {
         const int T0 = T * 16;
         const float2 bk = sgp->blk[T];
         uint2 vfr[NTW];
@@ -671,7 +705,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bf16x8_of(bv[nt], hi4(st[nt])), by, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        bf16x8_of(bv[nt], hi4(st[nt])), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     stage_y(T, nt, acc, sc);
                 }
             }
@@ -849,6 +883,44 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     };
 
+    // Outputs of one whole block on the block path from the true state h
+    // entering it; the state itself is not carried (the look-back launch's
+    // output sweep knows every block's entering state).
+    auto block_out = [&](const f32x4_t (&h)[NTW], int Bi) {
+        const float4 bk = sgp->blkB[Bi];
+        uint2 hh[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+            hh[nt] = make_uint2(pk_bf16(h[nt][0] * bk.x, h[nt][1] * bk.x), pk_bf16(h[nt][2] * bk.x, h[nt][3] * bk.x));
+        uint2 bvh[NB][NTW];
+        const uint2 z2 = make_uint2(0u, 0u);
+#pragma unroll
+        for (int aa = 0; aa < NB; ++aa) {
+            const int T = Bi * NB + aa, T0 = T * 16;
+            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const uint2 vfr = load_vfrag(T, nt);
+                bvh[aa][nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr.x), b4.y * hi_f32(vfr.x)),
+                                         pk_bf16(b4.z * lo_f32(vfr.y), b4.w * hi_f32(vfr.y)));
+            }
+            const float sc = sgp->ag[T0 + col];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
+                                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                if (aa >= 1)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2), yB12,
+                        acc, 0, 0, 0);
+                if (aa >= 3)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa >= 3 ? aa - 3 : 0][nt], z2), yB3,
+                                                                 acc, 0, 0, 0);
+                stage_y(T, nt, acc, sc);
+            }
+        }
+    };
+
     // All positions of the staged chunk (n valid): whole blocks on the block
     // path, the others (ragged, or a clock span too large) sub-block by sub-block.
     auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) {
@@ -857,7 +929,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 block_fast(st, Bi, out, tr);
             } else {
                 const int tend = min(n, (Bi + 1) * BLK);
-                for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, out, tr);
+                for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, out, tr, lpA[NB - 1], l16);
             }
         }
     };
@@ -1001,44 +1073,19 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // zero entering state, or the true one for segment 0.  Sweep 2: outputs.
     // Each chunk step stages the chunk held in the register buffer and refills
     // it with the loads of the next chunk, which then overlap the arithmetic.
-    const bool has_succ = SEG && seg + 1 < nseg;
-
     f32x4_t st[NTW];
     float tr[4] = {1.f, 0.f, 1.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];   // segment 0: from state_in; others: zero
 
-    // end of sweep 1: publish, look back, restart from the true entering state
-    auto between_sweeps = [&]() {
-        if (seg == 0) {
-            publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
-        } else {
-            publish(plan.agg + (slot + seg) * (size_t)ROWS * P, st, FLAG_AGG, tr);
-            f32x4_t e[NTW];
-            lookback(e);
-            // inclusive = Lambda_seg * entering + aggregate
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                f32x4_t inc;
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    inc[i] = tr[i] * e[nt][i] - tr[i + 1] * e[nt][i + 1] + st[nt][i];
-                    inc[i + 1] = tr[i] * e[nt][i + 1] + tr[i + 1] * e[nt][i] + st[nt][i + 1];
-                }
-                st_in[nt] = e[nt];
-                st[nt] = inc;
-            }
-            publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];
-    };
-
     ChunkRegs rb;
     if (SEG) {
         // Segment: its (at most RES) chunks were requested up front and stay in LDS.
+        constexpr int NBC = LC / BLK;   // blocks per chunk
+        const bool has_succ = seg + 1 < nseg;
         if (!has_succ && seg > 0) {
-            // last segment: only the entering state is needed
+            // last segment: the entering state first, so that the first sweep
+            // already runs from the true state
             f32x4_t e[NTW];
             lookback(e);
 #pragma unroll
@@ -1055,22 +1102,98 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             }
         }
         __syncthreads();
-        if (has_succ) {
-            for (int i = 0; i < nck; ++i) {
+        // Sweep 1: the state through the segment from its entering state (zero,
+        // state_in for segment 0, the looked-back state for the last segment),
+        // recorded at every block start.
+        f32x4_t h0[C::RES][NBC][NTW];
+#pragma unroll
+        for (int i = 0; i < C::RES; ++i) {
+            if (i < nck) {
                 const int n = min(LC, L - (c_begin + i) * LC);
                 sgp = &stg[i];
-                chunk_pass(st, n, false, tr);
+#pragma unroll
+                for (int Bi = 0; Bi < NBC; ++Bi) {
+                    if (Bi * BLK < n) {
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt) h0[i][Bi][nt] = st[nt];
+                        if (sgp->blkB[Bi].w == 0.f) {
+                            block_fast(st, Bi, false, tr);
+                        } else {
+                            const int tend = min(n, (Bi + 1) * BLK);
+                            for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, false, tr, lpA[NB - 1], l16);
+                        }
+                    }
+                }
             }
-            between_sweeps();
         }
-        // sweep 2 from the resident chunks: each wave reads and overwrites only
-        // its own columns, so no barrier is needed between chunks
-        for (int i = 0; i < nck; ++i) {
-            const int t0 = (c_begin + i) * LC;
-            const int n = min(LC, L - t0);
-            sgp = &stg[i];
-            chunk_pass(st, n, true, tr);
-            store_y(t0, n);
+        // Publish, look back.  gc: the entering state carried to the current
+        // block by the transfers of the blocks before it; the true state at a
+        // block start is h0 + gc (gc = 0 where sweep 1 began from the true state).
+        f32x4_t gc[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) gc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (has_succ) {
+            if (seg == 0) {
+                publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
+            } else {
+                publish(plan.agg + (slot + seg) * (size_t)ROWS * P, st, FLAG_AGG, tr);
+                f32x4_t e[NTW];
+                lookback(e);
+                // inclusive = Lambda_seg * entering + aggregate
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const float ir = tr[i] * e[nt][i] - tr[i + 1] * e[nt][i + 1] + st[nt][i];
+                        const float ii = tr[i] * e[nt][i + 1] + tr[i + 1] * e[nt][i] + st[nt][i + 1];
+                        st[nt][i] = ir;
+                        st[nt][i + 1] = ii;
+                    }
+                    gc[nt] = e[nt];
+                }
+                publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
+            }
+        }
+        // Sweep 2: outputs from the resident chunks.  Each wave reads and
+        // overwrites only its own columns, so no barrier is needed between chunks.
+        make_out_constants();
+#pragma unroll
+        for (int i = 0; i < C::RES; ++i) {
+            if (i < nck) {
+                const int t0 = (c_begin + i) * LC;
+                const int n = min(LC, L - t0);
+                sgp = &stg[i];
+#pragma unroll
+                for (int Bi = 0; Bi < NBC; ++Bi) {
+                    if (Bi * BLK < n) {
+                        f32x4_t h[NTW];
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt) h[nt] = h0[i][Bi][nt] + gc[nt];
+                        const float4 bk = sgp->blkB[Bi];
+                        if (bk.w == 0.f) {
+                            block_out(h, Bi);
+                        } else {
+                            const bf16x8_t al_r = make_sub_al();
+                            float l16_r[4], trd[4] = {1.f, 0.f, 1.f, 0.f};
+                            make_l16(l16_r);
+                            const int tend = min(n, (Bi + 1) * BLK);
+                            for (int T = Bi * NB; T * 16 < tend; ++T) subblock(h, T, n, true, trd, al_r, l16_r);
+                        }
+                        // carry gc over this (whole) block: lambda^BLK e^{-span}
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+                            for (int q = 0; q < 4; q += 2) {
+                                const float lr = bk.z * lB[q], li = bk.z * lB[q + 1];
+                                const float gr = gc[nt][q], gi = gc[nt][q + 1];
+                                gc[nt][q] = lr * gr - li * gi;
+                                gc[nt][q + 1] = lr * gi + li * gr;
+                            }
+                        }
+                    }
+                }
+                store_y(t0, n);
+            }
         }
     } else {
         // Whole sequence or segment, streamed through one staging buffer.  The
