@@ -60,7 +60,7 @@ def _bind(so_path: str, prec: str):
     lib = ctypes.CDLL(so_path)
     fn = getattr(lib, f"essh_oracle_prefill_{prec}")
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p] * 10 + [ctypes.c_int]
+    fn.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p] * 11 + [ctypes.c_int]
     tu = getattr(lib, f"essh_oracle_threads_used_{prec}")
     tu.restype = ctypes.c_int
     return lib, fn, tu
@@ -91,12 +91,13 @@ def make_prefill(so_path=None, precision="f64"):
     bound = None if so_path is None else _bind(so_path, precision)
 
     def prefill(v, delta, g_w, g_r, rho, theta, c, K_T=None, state_in=None,
-                per_mode=None, y_out=None, nthreads=1, want_state=True):
+                per_mode=None, y_out=None, nthreads=1, want_state=True, zl=None):
         """Run the sequential recurrence over all positions of v.
 
         Arguments are real arrays (already upcast from bf16 where relevant):
           v [B,L,K,P]; delta, g_w, g_r [B,L,K] (per channel) or [B,L,K,m] (per mode);
-          rho, theta [K,m]; c [K,m,2]; state_in [B,K,m,2,P] or None (zero state).
+          rho, theta [K,m]; c [K,m,2]; state_in [B,K,m,2,P] or None (zero state);
+          zl [K,m] zero-lag correction coefficients (Eq. 24) or None (core readout).
         ``y_out`` may be passed to observe that channels k >= K_T are left untouched.
         Returns (y, state_out) with y [B,L,K,P] and state_out [B,K,m,2,P]; channels
         k >= K_T of both keep their initial contents (zeros unless y_out is given).
@@ -108,14 +109,14 @@ def make_prefill(so_path=None, precision="f64"):
         pm = (np.ndim(delta) == 4) if per_mode is None else per_mode
         kt = K if K_T is None else int(K_T)
         delta_, g_w_, g_r_ = _as(delta, dt), _as(g_w, dt), _as(g_r, dt)
-        rho_, theta_, c_ = _as(rho, dt), _as(theta, dt), _as(c, dt)
+        rho_, theta_, c_, zl_ = _as(rho, dt), _as(theta, dt), _as(c, dt), _as(zl, dt)
         s_in = _as(state_in, dt)
         y = np.zeros((B, L, K, P), dt) if y_out is None else y_out
         assert y.dtype == dt and y.flags.c_contiguous and y.shape == (B, L, K, P)
         st = np.zeros((B, K, m, 2, P), dt) if want_state else None
         fn = (bound or _lib(precision))[1]
         rc = fn(B, L, K, m, P, kt, int(bool(pm)),
-                _ptr(v), _ptr(delta_), _ptr(g_w_), _ptr(g_r_), _ptr(rho_), _ptr(theta_), _ptr(c_),
+                _ptr(v), _ptr(delta_), _ptr(g_w_), _ptr(g_r_), _ptr(rho_), _ptr(theta_), _ptr(c_), _ptr(zl_),
                 _ptr(s_in), _ptr(st), _ptr(y), int(nthreads))
         if rc != 0:
             raise RuntimeError(f"oracle prefill failed with code {rc}")
@@ -132,19 +133,20 @@ def threads_used(precision="f64") -> int:
     return _lib(precision)[2]()
 
 
-def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, precision="f64"):
+def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, precision="f64", zl=None):
     """One token through n_layers independent mixers (decode is Eq. 5 for one position).
 
     state [NL,B,K,m,2,P] (not modified); v [NL,B,K,P]; delta, g_w, g_r [NL,B,K];
-    rho, theta [NL,K,m]; c [NL,K,m,2].  Returns (y [NL,B,K,P], new_state).
-    Channels k >= K_T of the returned state keep their old values.
+    rho, theta [NL,K,m]; c [NL,K,m,2]; zl [NL,K,m] or None (zero-lag correction, Eq. 24).
+    Returns (y [NL,B,K,P], new_state).  Channels k >= K_T of the returned state keep
+    their old values.
     """
     run = prefill if precision == "f64" else prefill_f32
     NL = v.shape[0]
     ys, sts = [], []
     for l in range(NL):
         y, st = run(v[l][:, None], delta[l][:, None], g_w[l][:, None], g_r[l][:, None],
-                    rho[l], theta[l], c[l], K_T=K_T, state_in=state[l])
+                    rho[l], theta[l], c[l], K_T=K_T, state_in=state[l], zl=None if zl is None else zl[l])
         Kt = v.shape[2] if K_T is None else K_T
         st[:, Kt:] = state[l][:, Kt:]
         ys.append(y[:, 0])

@@ -23,6 +23,11 @@
  *   paper's own granularity, Eq. 5 / App. C.2).  h(-1) is state_in, or zero.
  *   Channels k >= K_T are neither read nor written (truncation, App. C.4).
  *
+ *   Optional zero-lag correction (App. C.3, Eq. 24): with coefficients
+ *   a [K,m], the output becomes
+ *     z(t) = y(t) - sum_j a_kj * g_r(t) * g_w(t) * kc_kj * v(t)
+ *   (kc = Re c); without them (NULL) the output is the core readout y.
+ *
  * Layouts (row-major):  v, y [B,L,K,P];  delta, g_w, g_r [B,L,K] or
  * [B,L,K,m];  rho, theta [K,m];  c [K,m,2] (re, im);  state [B,K,m,2,P]
  * (planar: real plane then imaginary plane).
@@ -80,7 +85,7 @@ int FN(essh_oracle_threads_used)(void) { return g_threads_used; }
  */
 int FN(essh_oracle_prefill)(int B, int L, int K, int m, int P, int K_T, int per_mode,
                             const real* v, const real* delta, const real* g_w, const real* g_r,
-                            const real* rho, const real* theta, const real* c,
+                            const real* rho, const real* theta, const real* c, const real* zl,
                             const real* state_in, real* state_out, real* y, int nthreads)
 {
     if (B < 0 || L < 0 || K < 1 || m < 1 || P < 1 || K_T < 1 || K_T > K) return -1;
@@ -134,6 +139,10 @@ int FN(essh_oracle_prefill)(int B, int L, int K, int m, int P, int K_T, int per_
                         cplx hn = lam * h[(size_t)j * P + p] + gw * vt[p];
                         h[(size_t)j * P + p] = hn;
                         acc[p] += gr * C_RE(cc * hn);
+                    }
+                    if (zl) {   /* Eq. 24: the lag-zero term of this mode, scaled by a */
+                        real zc = zl[(size_t)k * m + j] * gr * gw * c[((size_t)k * m + j) * 2];
+                        for (int p = 0; p < P; ++p) acc[p] -= zc * vt[p];
                     }
                 }
                 real* yt = y + row * P;

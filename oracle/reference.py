@@ -77,6 +77,44 @@ def real_form(v, delta, g_w, g_r, rho, theta, c, K_T=None, state_in=None):
     return y, st
 
 
+def zero_lag_jrec(v, delta, g_w, g_r, rho, theta, c, zl, K_T=None, state_in=None):
+    """The zero-lag corrected output (App. C.3, Eq. 24) by its equivalent recurrence.
+
+    App. C.3 rewrites the correction without touching the readout: with
+    b(t) = g_w(t) e1 v(t)^T and J(t) = H(t) - a b(t),
+      J(t) = A(t) J(t-1) + (1 - a) b(t) + a A(t) b(t-1),    b(-1) = 0,
+    and the corrected output is z(t) = sum_j g_r,j(t) J_j(t)^T kappa_j.  Real
+    2xP form as printed (A = rho e^{-delta} R(theta), kappa = (kc, -ks)).
+    Returns (z, state) with state = H(L-1) = J(L-1) + a b(L-1).
+    """
+    v = np.asarray(v, np.float64)
+    B, L, K, P = v.shape
+    m = np.shape(rho)[1]
+    K_T = K if K_T is None else K_T
+    dl, gw, gr = _ctrl(delta, m), _ctrl(g_w, m), _ctrl(g_r, m)
+    y = np.zeros_like(v)
+    st = np.zeros((B, K, m, 2, P))
+    for b in range(B):
+        for k in range(K_T):
+            J = np.zeros((m, 2, P)) if state_in is None else np.array(state_in[b, k], np.float64)
+            bprev = np.zeros((m, 2, P))
+            for t in range(L):
+                for j in range(m):
+                    a = float(zl[k][j])
+                    th = float(theta[k][j])
+                    R = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+                    A = float(rho[k][j]) * np.exp(-dl[b, t, k, j]) * R
+                    bt = np.zeros((2, P))
+                    bt[0] = gw[b, t, k, j] * v[b, t, k]
+                    J[j] = A @ J[j] + (1.0 - a) * bt + a * (A @ bprev[j])
+                    bprev[j] = bt
+                    kappa = np.array([c[k][j][0], -c[k][j][1]], np.float64)
+                    y[b, t, k] += gr[b, t, k, j] * (kappa @ J[j])
+            for j in range(m):
+                st[b, k, j] = J[j] + float(zl[k][j]) * bprev[j]
+    return y, st
+
+
 def chunked(v, delta, g_w, g_r, rho, theta, c, Lc, K_T=None, state_in=None):
     """Chunk decomposition of the scan (Sec. 4.3), derived from the transition product Eq. 6.
 

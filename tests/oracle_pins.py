@@ -187,6 +187,46 @@ def pin_chunked_equals_sequential(prefill, Lc=16, L=53, per_mode=False):
     return max(_nerr(y, yc), _nerr(st, sc)), 1e-12
 
 
+def pin_zero_lag_recurrence(prefill, per_mode=False):
+    """Zero-lag correction (Eq. 24) against the equivalent J recurrence of App. C.3.
+
+    The oracle subtracts a g_r g_w kc v from the core readout; the reference
+    never forms the core readout: it runs J(t) = A J(t-1) + (1-a) b(t) + a A b(t-1)
+    and reads J directly.  State in and out included; a ~ U(0, 1) around the
+    paper's initial value 1/2.
+    """
+    B, L, K, m, P = 2, 37, 3, 4, 5
+    x = _rand(31, B, L, K, m, P, per_mode=per_mode)
+    rng = np.random.default_rng(32)
+    zl = rng.uniform(0.0, 1.0, size=(K, m))
+    s0 = rng.normal(0, 1.0, size=(B, K, m, 2, P))
+    y, st = prefill(**x, zl=zl, state_in=s0)
+    yr, sr = reference.zero_lag_jrec(**x, zl=zl, state_in=s0)
+    return max(_nerr(y, yr), _nerr(st, sr)), 1e-12
+
+
+def pin_zero_lag_lti_fft(prefill):
+    """With a constant clock and unit gates the corrected mixer is a causal
+    convolution whose lag-zero tap is psi(0) - sum_j a_j kc_j (App. C.3: the
+    correction changes only the lag-zero coefficient); evaluated by rFFT."""
+    B, L, K, m, P = 2, 80, 3, 4, 6
+    x = _rand(33, B, L, K, m, P)
+    x["delta"] = np.zeros((B, L, K))
+    x["g_w"] = np.ones((B, L, K))
+    x["g_r"] = np.ones((B, L, K))
+    zl = np.random.default_rng(34).uniform(0.0, 1.0, size=(K, m))
+    y, _ = prefill(**x, zl=zl)
+    yf = np.zeros_like(y)
+    n = 2 * L
+    for k in range(K):
+        phi = reference.lti_kernel(x["rho"][k], x["theta"][k], x["c"][k], L, 0.0)
+        phi[0] -= float(np.sum(zl[k] * x["c"][k][:, 0]))
+        Hf = np.fft.rfft(phi, n)
+        Vf = np.fft.rfft(x["v"][:, :, k, :], n, axis=1)
+        yf[:, :, k, :] = np.fft.irfft(Vf * Hf[None, :, None], n, axis=1)[:, :L]
+    return _nerr(y, yf), 1e-12
+
+
 ALL_PINS = [
     ("closed_form_eq12", pin_closed_form_eq12, {}),
     ("closed_form_eq12_per_mode", pin_closed_form_eq12, {"per_mode": True}),
@@ -200,4 +240,7 @@ ALL_PINS = [
     ("state_bound_eq17", pin_state_bound_eq17, {}),
     ("chunked_eq6_Lc16", pin_chunked_equals_sequential, {"Lc": 16}),
     ("chunked_eq6_Lc8_per_mode", pin_chunked_equals_sequential, {"Lc": 8, "per_mode": True}),
+    ("zero_lag_recurrence_eq24", pin_zero_lag_recurrence, {}),
+    ("zero_lag_recurrence_eq24_per_mode", pin_zero_lag_recurrence, {"per_mode": True}),
+    ("zero_lag_lti_fft", pin_zero_lag_lti_fft, {}),
 ]

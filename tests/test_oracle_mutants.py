@@ -33,6 +33,9 @@ MUTANTS = [
     ("state_in_imag_dropped", "h0 = state_in[s + p] + I * state_in[s + P + p];", "h0 = state_in[s + p];"),
     ("per_mode_index", "size_t ci = per_mode ? row * m + j : row;", "size_t ci = per_mode ? row * m : row;"),
     ("imag_readout_dropped", "acc[p] += gr * C_RE(cc * hn);", "acc[p] += gr * C_RE(cc) * C_RE(hn);"),
+    ("zero_lag_sign", "acc[p] -= zc * vt[p];", "acc[p] += zc * vt[p];"),
+    ("zero_lag_read_gate_dropped", "real zc = zl[(size_t)k * m + j] * gr * gw", "real zc = zl[(size_t)k * m + j] * gw"),
+    ("zero_lag_imag_part", "* gr * gw * c[((size_t)k * m + j) * 2];", "* gr * gw * c[((size_t)k * m + j) * 2 + 1];"),
 ]
 
 
