@@ -205,7 +205,7 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
     state0 = state.clone()
 
     def step(s):
-        rc = essh.essh_mixer_decode_step(NL, dims, sv[s], sd[s], sgw[s], sgr[s], rho, theta, c, state, y[s])
+        rc = essh.essh_mixer_decode_step(NL, dims, sv[s], sd[s], sgw[s], sgr[s], rho, theta, c, None, state, y[s])
         assert rc == 0
 
     # kernel duration: HIP events around each launch (eager)

@@ -15,8 +15,13 @@
  *   h_kj(t)      = lambda_kj(t) * h_kj(t-1) + g_w(t) * v_k(t)       (per value p)
  *   y_k(t)       = sum_j g_r(t) * Re(c_kj * h_kj(t))                 (the core output z^core)
  *
+ * Optionally with the zero-lag correction of App. C.3 (Eq. 24), coefficients
+ * a_kj:  z_k(t) = y_k(t) - sum_j a_kj * g_r(t) * g_w(t) * kc_kj * v_k(t)
+ * (per-mode gates in that sum when the controls are per mode).  It changes
+ * only the lag-zero coefficient and adds no state.
+ *
  * Channels k >= K_T are never read, computed or written (tier truncation,
- * App. C.4 and D.2; Sec. 4.3 "without evaluating discarded channels").
+ * App. C.4 and D.2; Sec. 4.3).
  *
  * Conventions shared by every entry point
  *   - Every array pointer is a DEVICE pointer owned by the caller; the
@@ -32,12 +37,13 @@
  *       g_w, g_r        [B, L, K]   (or [B, L, K, m] if ctrl_per_mode) io dtype
  *       rho, theta      [K, m]                fp32, 0 < rho < 1
  *       c               [K, m, 2]             fp32, (re, im) = (kc, ks)
+ *       zl              [K, m]                fp32 zero-lag coefficients a, or NULL
  *       state           [B, K, m, 2, P]       fp32, real plane then imaginary plane
  *     The channel stride of every array is the full K even when K_T < K.
  *   - Clock and gate values are post-activation: the kernels apply neither
  *     softplus nor sigmoid (App. C.2 defines those projections upstream).
- *   - v, y, g_w, g_r, delta and state must be 16-byte aligned; rho, theta, c
- *     4-byte aligned.  P * sizeof(io dtype) must be a multiple of 16 bytes.
+ *   - v, y, g_w, g_r, delta and state must be 16-byte aligned; rho, theta, c,
+ *     zl 4-byte aligned.  P * sizeof(io dtype) must be a multiple of 16 bytes.
  */
 #ifndef ESSH_H
 #define ESSH_H
@@ -74,7 +80,7 @@ typedef struct {
 } essh_dims;
 
 /* ABI version of this header (major * 100 + minor). */
-#define ESSH_ABI_VERSION 100
+#define ESSH_ABI_VERSION 101
 int32_t essh_abi_version(void);
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -108,6 +114,7 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d);
  *
  *   v, delta, g_w, g_r   inputs, layouts above (read only for k < K_T)
  *   rho, theta, c        mode tables [K, m] / [K, m, 2]
+ *   zl                   zero-lag coefficients [K, m] (Eq. 24), or NULL: output z^core
  *   state_in             [B, K, m, 2, P] state entering position 0, or NULL for H = 0
  *   state_out            [B, K, m, 2, P] state after position L-1, or NULL;
  *                        may alias state_in.  Channels k >= K_T untouched.
@@ -132,7 +139,7 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d);
  */
 essh_status essh_mixer_prefill(const essh_dims* d,
                                const void* v, const float* delta, const void* g_w, const void* g_r,
-                               const float* rho, const float* theta, const float* c,
+                               const float* rho, const float* theta, const float* c, const float* zl,
                                const float* state_in, float* state_out, void* y,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -148,12 +155,13 @@ essh_status essh_mixer_prefill(const essh_dims* d,
  *   delta                [n_layers, B, K] (or [n_layers, B, K, m]) fp32
  *   g_w, g_r             [n_layers, B, K] (or [n_layers, B, K, m]) io dtype
  *   rho, theta           [n_layers, K, m] fp32;  c [n_layers, K, m, 2] fp32
+ *   zl                   [n_layers, K, m] fp32 zero-lag coefficients, or NULL
  *   state                [n_layers, B, K, m, 2, P] fp32, updated in place (k < K_T only)
  *   y                    [n_layers, B, K, P] io dtype; channels k >= K_T untouched
  */
 essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
                                    const void* v, const float* delta, const void* g_w, const void* g_r,
-                                   const float* rho, const float* theta, const float* c,
+                                   const float* rho, const float* theta, const float* c, const float* zl,
                                    float* state, void* y, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -77,6 +77,7 @@ decode_kernel(DecodeArgs a, int P) {
         const float pi = __shfl(my_i, base + j);
         const float cr = a.c[(tab + j) * 2 + 0];
         const float ci = a.c[(tab + j) * 2 + 1];
+        const float za = a.zl ? a.zl[tab + j] * cr : 0.f;   // zero-lag correction (Eq. 24)
         float e, w, g;
         if (PER_MODE) {
             const size_t cj = row * M + j;
@@ -93,7 +94,7 @@ decode_kernel(DecodeArgs a, int P) {
         const float ni = ai * hr[j] + ar * hi[j];
         hr[j] = nr;
         hi[j] = ni;
-        acc += g * (cr * nr - ci * ni);
+        acc += g * (cr * nr - ci * ni - za * w);
     }
     if (!PER_MODE) acc *= g_ch;
 

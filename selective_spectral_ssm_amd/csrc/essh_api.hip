@@ -65,7 +65,7 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d) {
 
 essh_status essh_mixer_prefill(const essh_dims* d,
                                const void* v, const float* delta, const void* g_w, const void* g_r,
-                               const float* rho, const float* theta, const float* c,
+                               const float* rho, const float* theta, const float* c, const float* zl,
                                const float* state_in, float* state_out, void* y,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     essh_status st = check_dims(d, true);
@@ -73,7 +73,7 @@ essh_status essh_mixer_prefill(const essh_dims* d,
     const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
     if (!v || !delta || !g_w || !g_r || !rho || !theta || !c || !y) return ESSH_ERR_INVALID_ARG;
     if (!aligned(v, 16) || !aligned(y, 16) || !aligned(delta, 4) || !aligned(g_w, io) || !aligned(g_r, io) ||
-        !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4))
+        !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4) || (zl && !aligned(zl, 4)))
         return ESSH_ERR_INVALID_ARG;
     if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return ESSH_ERR_INVALID_ARG;
     if ((d->P * io) % 16 != 0) return ESSH_ERR_UNSUPPORTED;
@@ -104,6 +104,7 @@ essh_status essh_mixer_prefill(const essh_dims* d,
     a.rho = rho;
     a.theta = theta;
     a.c = c;
+    a.zl = zl;
     a.state_in = state_in;
     a.state_out = state_out;
     a.y = y;
@@ -122,7 +123,7 @@ essh_status essh_mixer_prefill(const essh_dims* d,
 
 essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
                                    const void* v, const float* delta, const void* g_w, const void* g_r,
-                                   const float* rho, const float* theta, const float* c,
+                                   const float* rho, const float* theta, const float* c, const float* zl,
                                    float* state, void* y, hipStream_t stream) {
     essh_status st = check_dims(d, false);
     if (st != ESSH_OK) return st;
@@ -130,7 +131,7 @@ essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
     const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
     if (!v || !delta || !g_w || !g_r || !rho || !theta || !c || !state || !y) return ESSH_ERR_INVALID_ARG;
     if (!aligned(v, 16) || !aligned(y, 16) || !aligned(state, 16) || !aligned(delta, 4) || !aligned(g_w, io) ||
-        !aligned(g_r, io) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4))
+        !aligned(g_r, io) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4) || (zl && !aligned(zl, 4)))
         return ESSH_ERR_INVALID_ARG;
     if ((long long)n_layers * d->B * d->K * d->P > (1LL << 30)) return ESSH_ERR_UNSUPPORTED;
     if (d->B == 0) return ESSH_OK;
@@ -148,6 +149,7 @@ essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
     a.rho = rho;
     a.theta = theta;
     a.c = c;
+    a.zl = zl;
     a.state = state;
     a.y = y;
     return from_hip(launch_decode(a, d->m, d->P, d->io_dtype, stream));

@@ -49,6 +49,7 @@ struct PrefillArgs {
     const float* rho;
     const float* theta;
     const float* c;
+    const float* zl;          // zero-lag coefficients [K, m] (Eq. 24) or null
     const float* state_in;
     float* state_out;
     void* y;
@@ -66,6 +67,7 @@ struct DecodeArgs {
     const float* rho;
     const float* theta;
     const float* c;
+    const float* zl;          // zero-lag coefficients [n_layers, K, m] or null
     float* state;
     void* y;
 };

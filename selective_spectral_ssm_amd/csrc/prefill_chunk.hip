@@ -373,6 +373,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const float2 cp = sm.cpw[r][j], pd = sm.p16[d][j];
             s += cp.x * pd.x - cp.y * pd.y;
         }
+        // zero-lag correction (Eq. 24): with per-channel gates it lowers the
+        // lag-zero coefficient by sum_j a_j kc_j
+        if (tau == 0 && a.zl) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) s -= a.zl[k * M + j] * a.c[(k * M + j) * 2];
+        }
         sm.psi[tau] = s;
     }
     __syncthreads();

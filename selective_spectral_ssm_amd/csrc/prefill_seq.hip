@@ -36,7 +36,8 @@ prefill_seq_kernel(PrefillArgs a, int P) {
     IO* y = static_cast<IO*>(a.y);
 
     // Pole and readout of each mode: rho e^{i theta} and c.
-    float lr[M], li[M], cr[M], ci[M], hr[M], hi[M];
+    // za: a_j kc_j, the lag-zero term removed by the zero-lag correction (Eq. 24)
+    float lr[M], li[M], cr[M], ci[M], hr[M], hi[M], za[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) {
         const float r = a.rho[k * M + j];
@@ -46,6 +47,7 @@ prefill_seq_kernel(PrefillArgs a, int P) {
         li[j] = r * sn;
         cr[j] = a.c[(k * M + j) * 2 + 0];
         ci[j] = a.c[(k * M + j) * 2 + 1];
+        za[j] = a.zl ? a.zl[k * M + j] * cr[j] : 0.f;
         if (a.state_in) {
             const size_t s = ((((size_t)b * K + k) * M + j) * 2) * P + p;
             hr[j] = a.state_in[s];
@@ -102,7 +104,7 @@ prefill_seq_kernel(PrefillArgs a, int P) {
                     const float ni = ai * hr[j] + ar * hi[j];
                     hr[j] = nr;
                     hi[j] = ni;
-                    acc += crd[u][j] * (cr[j] * nr - ci[j] * ni);
+                    acc += crd[u][j] * (cr[j] * nr - ci[j] * ni - za[j] * w);
                 }
             } else {
                 const float e = expf(-cd[u][0]);
@@ -114,7 +116,7 @@ prefill_seq_kernel(PrefillArgs a, int P) {
                     const float ni = ai * hr[j] + ar * hi[j];
                     hr[j] = nr;
                     hi[j] = ni;
-                    acc += cr[j] * nr - ci[j] * ni;
+                    acc += cr[j] * nr - ci[j] * ni - za[j] * w;
                 }
                 acc *= crd[u][0];
             }

@@ -64,9 +64,9 @@ def lib():
         L.essh_prefill_workspace_bytes.restype = SZ
         L.essh_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
         L.essh_mixer_prefill.restype = ctypes.c_int
-        L.essh_mixer_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 11 + [SZ, P]
+        L.essh_mixer_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12 + [SZ, P]
         L.essh_mixer_decode_step.restype = ctypes.c_int
-        L.essh_mixer_decode_step.argtypes = [I32, ctypes.POINTER(Dims)] + [P] * 9 + [P]
+        L.essh_mixer_decode_step.argtypes = [I32, ctypes.POINTER(Dims)] + [P] * 10 + [P]
         _lib = L
     return _lib
 
@@ -120,18 +120,18 @@ def essh_prefill_workspace_bytes(dims: Dims) -> int:
     return int(lib().essh_prefill_workspace_bytes(ctypes.byref(dims)))
 
 
-def essh_mixer_prefill(dims: Dims, v, delta, g_w, g_r, rho, theta, c, state_in, state_out, y,
+def essh_mixer_prefill(dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state_in, state_out, y,
                        workspace=None, workspace_bytes: int = 0, stream=None) -> int:
     """Direct call; returns the status code (no exception) so tests can check error paths."""
     return lib().essh_mixer_prefill(ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w), _ptr(g_r),
-                                    _ptr(rho), _ptr(theta), _ptr(c), _ptr(state_in), _ptr(state_out),
+                                    _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl), _ptr(state_in), _ptr(state_out),
                                     _ptr(y), _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
-def essh_mixer_decode_step(n_layers: int, dims: Dims, v, delta, g_w, g_r, rho, theta, c, state, y,
+def essh_mixer_decode_step(n_layers: int, dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state, y,
                            stream=None) -> int:
     return lib().essh_mixer_decode_step(int(n_layers), ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w),
-                                        _ptr(g_r), _ptr(rho), _ptr(theta), _ptr(c), _ptr(state), _ptr(y),
+                                        _ptr(g_r), _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl), _ptr(state), _ptr(y),
                                         _stream(stream))
 
 
@@ -147,12 +147,12 @@ class Prefill:
     """
 
     def __init__(self, v, delta, g_w, g_r, rho, theta, c, K_T=None, Lc=0,
-                 state_in=None, want_state=True, y=None, stream=None):
+                 state_in=None, want_state=True, y=None, stream=None, zl=None):
         B, L, K, P = v.shape
         m = rho.shape[1]
         per_mode = delta.dim() == 4
         self.dims = make_dims(B, L, K, m, P, K_T, Lc, per_mode, "bf16" if v.dtype == torch.bfloat16 else "f32")
-        self.args = (v, delta, g_w, g_r, rho, theta, c)
+        self.args = (v, delta, g_w, g_r, rho, theta, c, zl)
         self.state_in = state_in
         self.y = y if y is not None else torch.empty_like(v)
         self.state_out = (torch.zeros((B, K, m, 2, P), dtype=torch.float32, device=v.device)
@@ -170,17 +170,18 @@ class Prefill:
         return self.y, self.state_out
 
 
-def prefill(v, delta, g_w, g_r, rho, theta, c, K_T=None, Lc=0, state_in=None, want_state=True, y=None):
-    """Chunked prefill of one mixer.  Returns (y, state_out or None)."""
-    return Prefill(v, delta, g_w, g_r, rho, theta, c, K_T, Lc, state_in, want_state, y).run()
+def prefill(v, delta, g_w, g_r, rho, theta, c, K_T=None, Lc=0, state_in=None, want_state=True, y=None, zl=None):
+    """Chunked prefill of one mixer (zl: zero-lag coefficients or None).  Returns (y, state_out or None)."""
+    return Prefill(v, delta, g_w, g_r, rho, theta, c, K_T, Lc, state_in, want_state, y, zl=zl).run()
 
 
-def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, y=None):
+def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, y=None, zl=None):
     """One token through n_layers mixers; state [NL,B,K,m,2,P] is updated in place.  Returns y."""
     NL, B, K, P = v.shape
     m = rho.shape[-1]
     dims = make_dims(B, 1, K, m, P, K_T, 0, delta.dim() == 4, "bf16" if v.dtype == torch.bfloat16 else "f32")
     if y is None:
         y = torch.empty_like(v)
-    _check(essh_mixer_decode_step(NL, dims, v, delta, g_w, g_r, rho, theta, c, state, y), "essh_mixer_decode_step")
+    _check(essh_mixer_decode_step(NL, dims, v, delta, g_w, g_r, rho, theta, c, zl, state, y),
+           "essh_mixer_decode_step")
     return y

@@ -33,7 +33,7 @@ def test_header_declares_the_binding_set():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), f"libessh.so does not export {name}"
-    assert lib.essh_abi_version() == 100
+    assert lib.essh_abi_version() == 101
 
 
 def test_status_strings(lib):
@@ -46,11 +46,12 @@ FAKE = 0x10000          # 16-byte-aligned stand-in address; never dereferenced o
 
 def _call(dims, **over):
     p = {k: FAKE for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c", "y")}
+    p["zl"] = None
     p.update(over)
     lib = essh.lib()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.essh_mixer_prefill(ctypes.byref(dims), vp(p["v"]), vp(p["delta"]), vp(p["g_w"]), vp(p["g_r"]),
-                                  vp(p["rho"]), vp(p["theta"]), vp(p["c"]), None, None, vp(p["y"]),
+                                  vp(p["rho"]), vp(p["theta"]), vp(p["c"]), vp(p["zl"]), None, None, vp(p["y"]),
                                   None, 0, None)
 
 
@@ -80,7 +81,8 @@ def test_prefill_rejects_null_pointers(lib, which):
     assert _call(d, **{which: None}) == essh.ESSH_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("which,addr", [("v", FAKE + 2), ("y", FAKE + 8), ("delta", FAKE + 2), ("g_w", FAKE + 1)])
+@pytest.mark.parametrize("which,addr", [("v", FAKE + 2), ("y", FAKE + 8), ("delta", FAKE + 2), ("g_w", FAKE + 1),
+                                        ("zl", FAKE + 2)])
 def test_prefill_rejects_misaligned(lib, which, addr):
     d = essh.make_dims(8, 2048, 24, 4, 64, 24, 64)
     assert _call(d, **{which: addr}) == essh.ESSH_ERR_INVALID_ARG
@@ -89,13 +91,15 @@ def test_prefill_rejects_misaligned(lib, which, addr):
 def test_decode_and_state_init_reject_bad_args(lib):
     d = essh.make_dims(1, 1, 32, 8, 128, 33, 0)
     f = ctypes.c_void_p(FAKE)
-    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 9), None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 10), None) == essh.ESSH_ERR_INVALID_ARG
     d.K_T = 32
-    assert lib.essh_mixer_decode_step(0, ctypes.byref(d), *([f] * 9), None) == essh.ESSH_ERR_INVALID_ARG
-    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 8), None, None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_decode_step(0, ctypes.byref(d), *([f] * 10), None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 9), None, None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 7), ctypes.c_void_p(FAKE + 2), f, f,
+                                      None) == essh.ESSH_ERR_INVALID_ARG   # misaligned zl
     assert lib.essh_state_init(None, 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
     assert lib.essh_state_init(ctypes.c_void_p(FAKE + 4), 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
-    assert lib.essh_mixer_prefill(None, *([f] * 11), 0, None) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_mixer_prefill(None, *([f] * 12), 0, None) == essh.ESSH_ERR_INVALID_ARG
 
 
 def test_workspace_query_is_total(lib):
@@ -109,7 +113,7 @@ def test_workspace_query_is_total(lib):
 def _call_ws(dims, ws, ws_bytes):
     p = [ctypes.c_void_p(FAKE)] * 7
     lib = essh.lib()
-    return lib.essh_mixer_prefill(ctypes.byref(dims), *p, None, None, ctypes.c_void_p(FAKE),
+    return lib.essh_mixer_prefill(ctypes.byref(dims), *p, None, None, None, ctypes.c_void_p(FAKE),
                                   None if ws is None else ctypes.c_void_p(ws), ws_bytes, None)
 
 

@@ -28,23 +28,25 @@ def _essh():
     return essh
 
 
-def run_gpu_prefill(inp, K_T, Lc=0, state_in=None, y_init=None):
+def run_gpu_prefill(inp, K_T, Lc=0, state_in=None, y_init=None, zl=None):
     import torch
     essh = _essh()
     d = device_inputs(inp)
     s_in = None if state_in is None else to_dev(np.ascontiguousarray(state_in, np.float32))
     y = None if y_init is None else y_init
+    zd = None if zl is None else to_dev(np.ascontiguousarray(zl, np.float32))
     y, st = essh.prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
-                         K_T=K_T, Lc=Lc, state_in=s_in, y=y)
+                         K_T=K_T, Lc=Lc, state_in=s_in, y=y, zl=zd)
     torch.cuda.synchronize()
     return y, st
 
 
-def check_prefill(name, inp, K_T, Lc=0, state_in=None):
-    log(f"{name}: prefill K_T={K_T} Lc={Lc} shape={inp['v'].shape} io={inp['io']}")
-    y, st = run_gpu_prefill(inp, K_T, Lc, state_in)
+def check_prefill(name, inp, K_T, Lc=0, state_in=None, zl=None):
+    log(f"{name}: prefill K_T={K_T} Lc={Lc} shape={inp['v'].shape} io={inp['io']} zero-lag={zl is not None}")
+    y, st = run_gpu_prefill(inp, K_T, Lc, state_in, zl=zl)
     ox = oracle_inputs(inp)
-    y_ref, s_ref = oracle.prefill(**ox, K_T=K_T, state_in=state_in)
+    zo = None if zl is None else np.asarray(zl, np.float32).astype(np.float64)
+    y_ref, s_ref = oracle.prefill(**ox, K_T=K_T, state_in=state_in, zl=zo)
     tol = TOL[inp["io"]]
     ey = block_err(to_host_f64(y)[:, :, :K_T], y_ref[:, :, :K_T], chan_axis=2)
     es = block_err(to_host_f64(st)[:, :K_T], s_ref[:, :K_T], chan_axis=1)
@@ -93,6 +95,28 @@ def test_prefill_segment_scans(name, over, K_T):
     rng = np.random.default_rng(11)
     s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
     check_prefill(name, inp, K_T, 64, state_in=s0)
+
+
+# Zero-lag correction (App. C.3, Eq. 24) on every prefill path: the look-back
+# and whole-sequence MFMA kernels (per-channel bf16), the three-launch scan,
+# and the sequential kernel (fp32 io, per-mode controls).
+ZERO_LAG = [("lookback_bf16", 1, dict(B=5, L=64 * 9 + 5, K=8), 8, 64),
+            ("whole_seq_bf16", 1, dict(B=16, L=200, K=24), 24, 64),
+            ("three_launch_bf16", 4, dict(L=1500), 6, 128),
+            ("sequential_f32", 0, {}, 8, 0),
+            ("sequential_per_mode", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
+
+
+@pytest.mark.parametrize("name,widx,over,K_T,Lc", ZERO_LAG, ids=[c[0] for c in ZERO_LAG])
+def test_prefill_zero_lag(name, widx, over, K_T, Lc):
+    over = dict(over)
+    per_mode = over.pop("per_mode", False)
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w, per_mode=per_mode)
+    rng = np.random.default_rng(21)
+    zl = rng.uniform(0.0, 1.0, size=(w.K, w.m)).astype(np.float32)
+    s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    check_prefill(name, inp, K_T, Lc, state_in=s0, zl=zl)
 
 
 def test_prefill_state_in_out():
@@ -179,7 +203,7 @@ def test_prefill_workspace_reuse_and_state_alias():
     y2 = torch.empty_like(d["v"])
     ws = torch.zeros(call.ws_bytes, dtype=torch.uint8, device="cuda")
     rc = essh.essh_mixer_prefill(call.dims, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
-                                 state, state, y2, ws, call.ws_bytes)
+                                 None, state, state, y2, ws, call.ws_bytes)
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(y2, ys[0][0]) and torch.equal(state, ys[0][1])
@@ -209,7 +233,7 @@ def test_prefill_truncation_bit_identical_and_untouched():
         nws = essh.essh_prefill_workspace_bytes(dims)
         ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device="cuda")
         st = essh.essh_mixer_prefill(dims, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"],
-                                     d["c"], None, s_sent, sentinel, ws, nws)
+                                     d["c"], None, None, s_sent, sentinel, ws, nws)
         assert st == 0
         torch.cuda.synchronize()
         assert torch.equal(sentinel[:, :, :K_T], y_full[:, :, :K_T])
@@ -234,11 +258,11 @@ def test_prefill_empty_inputs():
     s_out = torch.zeros_like(s_in)
     y = torch.empty((2, 1, 3, w.P), dtype=torch.bfloat16, device="cuda")  # unused, must be non-null
     assert essh.essh_mixer_prefill(dims, v if v.numel() else y, dl if dl.numel() else tab, g if g.numel() else y,
-                                   g if g.numel() else y, tab, tab, c, s_in, s_out, y) == 0
+                                   g if g.numel() else y, tab, tab, c, None, s_in, s_out, y) == 0
     torch.cuda.synchronize()
     assert torch.equal(s_out, s_in)
     dims0 = essh.make_dims(0, 5, 3, w.m, w.P, 3, 64)
-    assert essh.essh_mixer_prefill(dims0, y, tab, y, y, tab, tab, c, None, None, y) == 0
+    assert essh.essh_mixer_prefill(dims0, y, tab, y, y, tab, tab, c, None, None, None, y) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -291,16 +315,18 @@ def test_decode_step_matches_oracle(io, per_mode, m, P):
     import torch
     essh = _essh()
     inp, state = _decode_case(3, 2, 6, m, P, io, per_mode)
-    for K_T in (2, 6):
-        log(f"decode io={io} per_mode={per_mode} m={m} P={P} K_T={K_T}")
+    zl = np.random.default_rng(9).uniform(0.0, 1.0, size=(3, 6, m)).astype(np.float32)
+    for K_T, zero_lag in ((2, False), (6, False), (6, True)):
+        log(f"decode io={io} per_mode={per_mode} m={m} P={P} K_T={K_T} zero-lag={zero_lag}")
         d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
         st = to_dev(state.copy())
         y = torch.full_like(d["v"], 3.0)
         essh.decode_step(st, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
-                         K_T=K_T, y=y)
+                         K_T=K_T, y=y, zl=to_dev(zl) if zero_lag else None)
         torch.cuda.synchronize()
         ox = {k: I.as_f64(inp[k], io) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
-        y_ref, s_ref = oracle.decode_step(state.astype(np.float64), **ox, K_T=K_T)
+        y_ref, s_ref = oracle.decode_step(state.astype(np.float64), **ox, K_T=K_T,
+                                          zl=zl.astype(np.float64) if zero_lag else None)
         tol = TOL[io]
         ey = block_err(to_host_f64(y)[:, :, :K_T].reshape(-1, K_T, P), y_ref[:, :, :K_T].reshape(-1, K_T, P), 1)
         es = block_err(to_host_f64(st)[:, :, :K_T].reshape(-1, K_T, m * 2 * P),
