@@ -251,7 +251,7 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
                 frac_of_hbm_peak=nbytes / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
-def cpu_baseline(inp, w, K_T, budget_s=10.0, max_runs=200):
+def cpu_baseline(inp, w, K_T, budget_s=10.0, max_runs=2000):
     """The fp64 CPU oracle, as the parity tests use it, on the whole main workload.
 
     The workload takes a small fraction of a second on the host, so the sample
