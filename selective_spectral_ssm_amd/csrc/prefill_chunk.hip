@@ -298,30 +298,49 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     float ecd[SPW][C::CPL];
     uint32_t ecw[SPW][C::CPL], ecr[SPW][C::CPL];
     const int nck = c_end - c_begin;
+
+    // Mode-table inputs of this thread's pole-table entries (and of the
+    // zero-lag term), requested before the tile copies so that the tables can
+    // be built while the copies are in flight.
+    constexpr int NPOLE = (18 + C::NB) * M;
+    constexpr int NPIT = (NPOLE + C::THREADS - 1) / C::THREADS;
+    float tb_r[NPIT], tb_th[NPIT], tb_cr[NPIT], tb_ci[NPIT];
+#pragma unroll
+    for (int it = 0; it < NPIT; ++it) {
+        const int idx = min(tid + it * C::THREADS, NPOLE - 1);
+        const int id2 = idx >= 17 * M ? idx - 17 * M : idx;
+        const int j = id2 % M;
+        tb_r[it] = a.rho[k * M + j];
+        tb_th[it] = a.theta[k * M + j];
+        tb_cr[it] = a.c[(k * M + j) * 2];
+        tb_ci[it] = a.c[(k * M + j) * 2 + 1];
+    }
+    float zl_a[M], zl_kc[M];   // a_j and kc_j of the zero-lag term (Eq. 24)
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        zl_a[j] = a.zl ? a.zl[k * M + j] : 0.f;
+        zl_kc[j] = a.c[(k * M + j) * 2];
+    }
+
+    // Every control row is requested (positions past the segment or past L
+    // repeat a valid row, whose values only reach positions that are never
+    // written), so no loaded value is merged with a default and nothing waits
+    // for these loads before the tile copies are issued.
     if (SEG) {
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
             const int i = q * C::NW + wave;
-            if (i < nck) {
 #pragma unroll
-                for (int u = 0; u < C::CPL; ++u) {
-                    const int rr = lane * C::CPL + u;
-                    const int t = (c_begin + i) * LC + rr;
-                    if (rr < LC && t < L) {
-                        const size_t row = ((size_t)b * L + t) * K + k;
-                        ecd[q][u] = a.delta[row];
-                        ecw[q][u] = gwg[row];
-                        ecr[q][u] = grg[row];
-                    } else {
-                        ecd[q][u] = 0.f;
-                        ecw[q][u] = 0u;
-                        ecr[q][u] = 0u;
-                    }
-                }
+            for (int u = 0; u < C::CPL; ++u) {
+                const int rr = min(lane * C::CPL + u, LC - 1);
+                const int t = min((c_begin + i) * LC + rr, L - 1);
+                const size_t row = ((size_t)b * L + t) * K + k;
+                ecd[q][u] = a.delta[row];
+                ecw[q][u] = gwg[row];
+                ecr[q][u] = grg[row];
             }
         }
     }
-    constexpr int NPOLE = (18 + C::NB) * M;
     if (SEG) {
         constexpr int UPR = P / 8;                 // 16-byte units per tile row
         constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
@@ -344,13 +363,16 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     }
 
     // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16, lambda^{16 d} ---------
-    for (int idx = tid; idx < NPOLE; idx += C::THREADS) {
+#pragma unroll
+    for (int it = 0; it < NPIT; ++it) {
+        const int idx = tid + it * C::THREADS;
+        if (idx >= NPOLE) break;
         const bool blk16 = idx >= 17 * M;
         const int id2 = blk16 ? idx - 17 * M : idx;
         const int i0 = id2 / M, j = id2 - i0 * M;
         const int tau = blk16 ? 16 * i0 : i0;
-        const float r = a.rho[k * M + j];
-        const float th = a.theta[k * M + j];
+        const float r = tb_r[it];
+        const float th = tb_th[it];
         const float mag = tau == 0 ? 1.f : exp2f((float)tau * log2f(r));
         float sn, cs;
         sincosf(th * (float)tau, &sn, &cs);   // |theta tau| <= 64 pi
@@ -359,7 +381,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             sm.p16[i0][j] = make_float2(pr, pi);
         } else {
             sm.pw[tau][j] = make_float2(pr, pi);
-            const float cr = a.c[(k * M + j) * 2], ci = a.c[(k * M + j) * 2 + 1];
+            const float cr = tb_cr[it], ci = tb_ci[it];
             sm.cpw[tau][j] = make_float2(cr * pr - ci * pi, cr * pi + ci * pr);
         }
     }
@@ -375,9 +397,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
         // zero-lag correction (Eq. 24): with per-channel gates it lowers the
         // lag-zero coefficient by sum_j a_j kc_j
-        if (tau == 0 && a.zl) {
+        if (tau == 0) {
 #pragma unroll
-            for (int j = 0; j < M; ++j) s -= a.zl[k * M + j] * a.c[(k * M + j) * 2];
+            for (int j = 0; j < M; ++j) s -= zl_a[j] * zl_kc[j];
         }
         sm.psi[tau] = s;
     }
