@@ -62,6 +62,8 @@
 //   * Look-back messages are written and read with agent-scope atomic
 //     accesses (they bypass the per-XCD L2), flags carry a per-launch epoch,
 //     and every wait is bounded.
+#include <type_traits>
+
 #include "essh_internal.h"
 
 namespace essh {
@@ -72,6 +74,8 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// Read-only fp32 data addressed uniformly across a workgroup (constant address space).
+typedef const __attribute__((address_space(4))) float* cfloat_p;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -135,28 +139,40 @@ struct Cfg {
     static_assert(LC % 32 == 0 && LC <= 128, "chunk length must be 32, 64 or 128");
     static_assert(M >= 1 && M <= 8, "1..8 modes");
     static_assert(LC % RPI == 0, "v tile loads must tile the chunk");
+    static_assert(RES >= 1 && RES <= 4, "one to four resident chunks");
 };
 
 // Per-chunk staged data.
 template <class C>
 struct __align__(16) Stage {
-    float q2[C::LC];                 // chunk-local inclusive clock sum * log2(e)
-    float gw[C::LC];                 // write gate
-    float gr[C::LC];                 // read gate
+    float q2[C::LC];                 // chunk-local inclusive clock sum * log2(e) (the raw clock
+                                     // while the segmented scan's copies are staged)
     float bq[C::LC];                 // b(s) = e^{qh(s)-qh(T0-1)} g_w(s)   (0 beyond the chunk)
     float ag[C::LC];                 // a(t) g_r(t) = e^{-(qh(t)-qh(T0-1))} g_r(t)
     float2 blk[C::NSB];              // per sub-block: (A_T, 1 if the exact path is needed)
     float4 blkB[C::LC / 32];         // per block: (H_s, A_e, Lambda_e, 1 if the sub-block path is needed);
                                      // Lambda_e = e^{-clock span} also on the sub-block path
-    alignas(16) uint16_t V[C::LC * C::P];   // v tile [t][P] (swizzled units); y staged in place
+    // Gates as bf16 bits in the low half of a 32-bit slot: a global-to-LDS copy
+    // of 16-bit elements writes one 32-bit slot per lane.
+    uint32_t gw[C::LC];              // write gate
+    uint32_t gr[C::LC];              // read gate
+};
+
+// v tile of a staged chunk: [t][P] bf16 (swizzled units); y is staged in place.
+template <class C>
+struct __align__(16) VTile {
+    uint16_t V[C::LC * C::P];
 };
 
 template <class C>
 struct __align__(16) Smem {
-    float2 pw[17][C::M];             // lambda_j^tau, tau = 0..16
+    // lambda_j^tau, tau = 0..16, then (rows 17 + d) lambda_j^{16 d}, d = 0..NB: one
+    // array, so that both kinds of entry are written by one store whose target
+    // the compiler can still tell apart from the asynchronous tile copies
+    float2 pw[17 + C::NB + 1][C::M];
     float2 cpw[17][C::M];            // c_j lambda_j^tau
-    float2 p16[C::NB + 1][C::M];     // lambda_j^{16 d}, d = 0..NB
     float psi[C::BLK];               // sum_j Re(c_j lambda_j^tau), tau = 0..BLK-1
+    float4 mtab[C::M];               // (rho_j, theta_j, Re c_j, Im c_j) of the channel
     int ticket;
     unsigned epoch;
     int lb_cnt;
@@ -182,6 +198,36 @@ __device__ __forceinline__ void wait_stores_complete() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations, not for its outstanding vector memory operations (a full
+// __syncthreads also waits for asynchronous global-to-LDS copies still in
+// flight).
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most N of this wave's vector memory operations are outstanding
+// (they complete in issue order for this counter).
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Calls f(std::integral_constant<int, I>()) for I = B .. E-1 in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
 }
 
 __device__ __forceinline__ void st_agent(float* p, float x) {
@@ -230,7 +276,14 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // The staged chunks are an LDS object of their own, so that accesses to
     // the tables in sm are not ordered behind the asynchronous tile copies.
     __shared__ Smem<C> sm;
-    __shared__ Stage<C> stg[MODE == MODE_LOOKBACK ? C::RES : 1];
+    // Each resident chunk's factors and v tile are LDS objects of their own:
+    // the compiler orders a read of one only behind the asynchronous copies
+    // into that object, so a chunk can be read while later chunks' copies
+    // are still in flight.  Objects a launch mode never indexes are dropped.
+    __shared__ Stage<C> sc0, sc1, sc2, sc3;
+    __shared__ VTile<C> sv0, sv1, sv2, sv3;
+    auto stage_c = [&](int i) -> Stage<C>* { return i == 0 ? &sc0 : i == 1 ? &sc1 : i == 2 ? &sc2 : &sc3; };
+    auto stage_v = [&](int i) -> uint16_t* { return i == 0 ? sv0.V : i == 1 ? sv1.V : i == 2 ? sv2.V : sv3.V; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -288,65 +341,63 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const uint16_t* grg = static_cast<const uint16_t*>(a.g_r);
     uint16_t* yg = static_cast<uint16_t*>(a.y);
 
-    // ---- segmented scan: every chunk of the segment is requested at once -------------------
-    // The controls (wave w holds those of resident chunks w, w + NW, ...; the
-    // gates as raw bf16 bits), then the v tiles straight into their LDS stage
-    // buffers (global_load_lds, 16 bytes per lane; a wave instruction fills 1
-    // KB of the tile, so each lane fetches the 16-byte unit whose swizzled
-    // slot is lane-th of that block).
-    constexpr int SPW = (C::RES + C::NW - 1) / C::NW;   // resident chunks per wave
-    float ecd[SPW][C::CPL];
-    uint32_t ecw[SPW][C::CPL], ecr[SPW][C::CPL];
     const int nck = c_end - c_begin;
 
-    // Mode-table inputs of this thread's pole-table entries (and of the
-    // zero-lag term), requested before the tile copies so that the tables can
-    // be built while the copies are in flight.
+    // Mode tables of channel k and the zero-lag coefficients, read through the
+    // scalar cache (the channel is the same for the whole workgroup).  Scalar
+    // loads are counted apart from vector memory operations, so building the
+    // tables does not wait for the tile copies below.
     constexpr int NPOLE = (18 + C::NB) * M;
-    constexpr int NPIT = (NPOLE + C::THREADS - 1) / C::THREADS;
-    float tb_r[NPIT], tb_th[NPIT], tb_cr[NPIT], tb_ci[NPIT];
+    float m_rho[M], m_th[M], m_cr[M], m_ci[M], m_za[M];
+    {
+        const cfloat_p rho_s = (cfloat_p)(a.rho) + k * M;
+        const cfloat_p th_s = (cfloat_p)(a.theta) + k * M;
+        const cfloat_p c_s = (cfloat_p)(a.c) + 2 * k * M;
+        const cfloat_p zl_s = (cfloat_p)(a.zl ? a.zl : a.rho) + k * M;   // never a null base
 #pragma unroll
-    for (int it = 0; it < NPIT; ++it) {
-        const int idx = min(tid + it * C::THREADS, NPOLE - 1);
-        const int id2 = idx >= 17 * M ? idx - 17 * M : idx;
-        const int j = id2 % M;
-        tb_r[it] = a.rho[k * M + j];
-        tb_th[it] = a.theta[k * M + j];
-        tb_cr[it] = a.c[(k * M + j) * 2];
-        tb_ci[it] = a.c[(k * M + j) * 2 + 1];
-    }
-    float zl_a[M], zl_kc[M];   // a_j and kc_j of the zero-lag term (Eq. 24)
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-        zl_a[j] = a.zl ? a.zl[k * M + j] : 0.f;
-        zl_kc[j] = a.c[(k * M + j) * 2];
-    }
-
-    // Every control row is requested (positions past the segment or past L
-    // repeat a valid row, whose values only reach positions that are never
-    // written), so no loaded value is merged with a default and nothing waits
-    // for these loads before the tile copies are issued.
-    if (SEG) {
-#pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            const int i = q * C::NW + wave;
-#pragma unroll
-            for (int u = 0; u < C::CPL; ++u) {
-                const int rr = min(lane * C::CPL + u, LC - 1);
-                const int t = min((c_begin + i) * LC + rr, L - 1);
-                const size_t row = ((size_t)b * L + t) * K + k;
-                ecd[q][u] = a.delta[row];
-                ecw[q][u] = gwg[row];
-                ecr[q][u] = grg[row];
-            }
+        for (int j = 0; j < M; ++j) {
+            m_rho[j] = rho_s[j];
+            m_th[j] = th_s[j];
+            m_cr[j] = c_s[2 * j];
+            m_ci[j] = c_s[2 * j + 1];
+            m_za[j] = a.zl ? zl_s[j] : 0.f;
         }
     }
+
+    // ---- segmented scan: every chunk of the segment is requested at once -------------------
+    // Asynchronous global-to-LDS copies only (no register loads): first the
+    // controls of every resident chunk (clock into q2, gate bits into gw/gr;
+    // 64 positions per wave instruction, spread over the waves), then the v
+    // tiles (16 bytes per lane; a wave instruction fills 1 KB of the tile, so
+    // each lane fetches the 16-byte unit whose swizzled slot is lane-th of that
+    // block).  Every wave issues the same number of tile copies per chunk, TLW,
+    // after all control copies, so "chunk i has landed" is "at most
+    // (RES-1-i) * TLW copies outstanding" in every wave.  Rows past the
+    // segment or past L repeat a valid row; their values only reach positions
+    // that are never written.
+    constexpr int UPR = P / 8;                 // 16-byte units per tile row
+    constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
+    static_assert(INSTR % C::NW == 0, "tile instructions must divide over the waves");
+    constexpr int TLW = INSTR / C::NW;         // tile copies per wave and chunk
     if (SEG) {
-        constexpr int UPR = P / 8;                 // 16-byte units per tile row
-        constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
-        static_assert(INSTR % C::NW == 0, "tile instructions must divide over the waves");
-        // all RES stages are requested (rows past the segment's last chunk
-        // repeat a valid row), so the count of these loads is fixed
+        constexpr int CIA = (LC + 63) / 64;    // instructions per control array of a chunk
+        constexpr int NCI = C::RES * 3 * CIA;
+#pragma unroll
+        for (int ci = 0; ci < NCI; ++ci) {
+            const int i = ci / (3 * CIA), arr = (ci / CIA) % 3, u = ci % CIA;
+            const int pos = u * 64 + lane;
+            if (ci % C::NW == wave && pos < LC) {
+                const int t = min((c_begin + i) * LC + pos, L - 1);
+                const size_t row = ((size_t)b * L + t) * K + k;
+                Stage<C>* sp = stage_c(i);
+                if (arr == 0)
+                    __builtin_amdgcn_global_load_lds(a.delta + row, (lds_void_t*)(&sp->q2[u * 64]), 4, 0, 0);
+                else if (arr == 1)   // 16-bit element -> 32-bit slot per lane
+                    __builtin_amdgcn_global_load_lds(gwg + row, (lds_void_t*)(&sp->gw[u * 64]), 2, 0, 0);
+                else
+                    __builtin_amdgcn_global_load_lds(grg + row, (lds_void_t*)(&sp->gr[u * 64]), 2, 0, 0);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < C::RES; ++i) {
 #pragma unroll
@@ -357,53 +408,54 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int u = pu ^ (((r / C::RP256) & C::SWZ_MASK) << 1);
                 const int t = min((c_begin + i) * LC + r, L - 1);   // rows past L: any valid row
                 const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&stg[i].V[ins * 512]), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_v(i) + ins * 512), 16, 0, 0);
             }
         }
     }
 
     // ---- pole tables: lambda^tau and c lambda^tau for tau = 0..16, lambda^{16 d} ---------
+    // (LDS-only barriers here: the tile copies stay in flight.)
 #pragma unroll
-    for (int it = 0; it < NPIT; ++it) {
-        const int idx = tid + it * C::THREADS;
-        if (idx >= NPOLE) break;
+    for (int j = 0; j < M; ++j)
+        if (tid == j) sm.mtab[j] = make_float4(m_rho[j], m_th[j], m_cr[j], m_ci[j]);
+    lds_barrier();
+    for (int idx = tid; idx < NPOLE; idx += C::THREADS) {
         const bool blk16 = idx >= 17 * M;
         const int id2 = blk16 ? idx - 17 * M : idx;
         const int i0 = id2 / M, j = id2 - i0 * M;
         const int tau = blk16 ? 16 * i0 : i0;
-        const float r = tb_r[it];
-        const float th = tb_th[it];
+        const float4 mt = sm.mtab[j];
+        const float r = mt.x;
+        const float th = mt.y;
         const float mag = tau == 0 ? 1.f : exp2f((float)tau * log2f(r));
         float sn, cs;
         sincosf(th * (float)tau, &sn, &cs);   // |theta tau| <= 64 pi
         const float pr = mag * cs, pi = mag * sn;
-        if (blk16) {
-            sm.p16[i0][j] = make_float2(pr, pi);
-        } else {
-            sm.pw[tau][j] = make_float2(pr, pi);
-            const float cr = tb_cr[it], ci = tb_ci[it];
+        sm.pw[blk16 ? 17 + i0 : tau][j] = make_float2(pr, pi);
+        if (!blk16) {
+            const float cr = mt.z, ci = mt.w;
             sm.cpw[tau][j] = make_float2(cr * pr - ci * pi, cr * pi + ci * pr);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // psi(16 d + r) = sum_j Re(c_j lambda_j^r lambda_j^{16 d})
     for (int tau = tid; tau < C::BLK; tau += C::THREADS) {
         const int d = tau >> 4, r = tau & 15;
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < M; ++j) {
-            const float2 cp = sm.cpw[r][j], pd = sm.p16[d][j];
+            const float2 cp = sm.cpw[r][j], pd = sm.pw[17 + d][j];
             s += cp.x * pd.x - cp.y * pd.y;
         }
         // zero-lag correction (Eq. 24): with per-channel gates it lowers the
         // lag-zero coefficient by sum_j a_j kc_j
         if (tau == 0) {
 #pragma unroll
-            for (int j = 0; j < M; ++j) s -= zl_a[j] * zl_kc[j];
+            for (int j = 0; j < M; ++j) s -= m_za[j] * m_cr[j];
         }
         sm.psi[tau] = s;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- per-lane constant MFMA operands ------------------------------------------------
     // Output product of target sub-block a of a block (B operands; lane (g, col)
@@ -438,7 +490,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int row = 4 * g + i, j = row >> 1;
                 float val = 0.f;
                 if (j < M) {
-                    const float2 cp = sm.cpw[col + 1][j < M ? j : 0], pd = sm.p16[aa][j < M ? j : 0];
+                    const float2 cp = sm.cpw[col + 1][j < M ? j : 0], pd = sm.pw[17 + aa][j < M ? j : 0];
                     val = (row & 1) ? -(cp.x * pd.y + cp.y * pd.x) : (cp.x * pd.x - cp.y * pd.y);
                 }
                 h[4 + i] = f32_to_bf16(val);
@@ -468,7 +520,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 float val = 0.f;
                 if (jr < M) {
                     const float2 pw = sm.pw[15 - 4 * g - e][jr < M ? jr : 0];
-                    const float2 pd = sm.p16[NB - 1 - aa][jr < M ? jr : 0];
+                    const float2 pd = sm.pw[17 + NB - 1 - aa][jr < M ? jr : 0];
                     val = (col & 1) ? (pw.x * pd.y + pw.y * pd.x) : (pw.x * pd.x - pw.y * pd.y);
                 }
                 const uint16_t hb = f32_to_bf16(val);
@@ -480,8 +532,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * g + hh;
-            const float2 pb = j < M ? sm.p16[NB][j < M ? j : 0] : make_float2(0.f, 0.f);
-            const float2 p1 = j < M ? sm.p16[1][j < M ? j : 0] : make_float2(0.f, 0.f);
+            const float2 pb = j < M ? sm.pw[17 + NB][j < M ? j : 0] : make_float2(0.f, 0.f);
+            const float2 p1 = j < M ? sm.pw[17 + 1][j < M ? j : 0] : make_float2(0.f, 0.f);
             lB[2 * hh] = pb.x;
             lB[2 * hh + 1] = pb.y;
             l16[2 * hh] = p1.x;
@@ -510,7 +562,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * g + hh;
-            const float2 p1 = j < M ? sm.p16[1][j < M ? j : 0] : make_float2(0.f, 0.f);
+            const float2 p1 = j < M ? sm.pw[17 + 1][j < M ? j : 0] : make_float2(0.f, 0.f);
             o[2 * hh] = p1.x;
             o[2 * hh + 1] = p1.y;
         }
@@ -519,34 +571,41 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     if (!SEG) make_out_constants();
 
     // ---- state in the accumulator layout ---------------------------------------------
-    // st_in: the entering state.  Segment 0 of a whole-sequence or look-back
-    // launch reads state_in once up front, so that an aliasing state_out
-    // written by the last segment cannot race with it.  In the three-launch
-    // scan the aggregate launch copies state_in into the entering-state slot
-    // of segment 0 and the streaming launch reads only those slots.
+    // The entering state.  Segment 0 reads state_in before any segment of the
+    // sequence can finish (a look-back segment before it publishes its
+    // inclusive state, which the last segment waits for), so that an aliasing
+    // state_out written by the last segment cannot race with it.  In the
+    // three-launch scan the aggregate launch copies state_in into the
+    // entering-state slot of segment 0 and the streaming launch reads only
+    // those slots.  The look-back launch reads it after its first sweep, so
+    // that no register load is outstanding while its tile copies land.
     const bool split_stream = MODE == MODE_STREAM && nseg > 1;
-    f32x4_t st_in[NTW];
+    auto load_entering = [&](f32x4_t (&x)[NTW]) {
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int p = wave * WCOLS + nt * 16 + col;
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = wave * WCOLS + nt * 16 + col;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * g + i, j = row >> 1, cmp = row & 1;
-            float x = 0.f;
-            if (split_stream) {
-                if (row < ROWS) x = plan.incl[((slot + seg) * ROWS + row) * (size_t)P + p];
-            } else if (seg == 0 && a.state_in && j < M) {
-                x = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i, j = row >> 1, cmp = row & 1;
+                float v = 0.f;
+                if (split_stream) {
+                    if (row < ROWS) v = plan.incl[((slot + seg) * ROWS + row) * (size_t)P + p];
+                } else if (seg == 0 && a.state_in && j < M) {
+                    v = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
+                }
+                x[nt][i] = v;
             }
-            st_in[nt][i] = x;
         }
-    }
+    };
+    f32x4_t st_in[NTW];
+    if (!SEG) load_entering(st_in);
 
     // ---- chunk pipeline helpers ---------------------------------------------------------
     const int vrow_l = lane / C::LPR;          // row of this lane inside a wave load
     const int vunit = lane % C::LPR;           // 16-byte unit of this lane inside a row
     const size_t vcol0 = (size_t)wave * WCOLS + vunit * 8;
-    Stage<C>* sgp = &stg[0];   // staged chunk the helpers work on
+    Stage<C>* sgp = stage_c(0);   // staged chunk the helpers work on: factors
+    uint16_t* sgv = stage_v(0);   // ... and v tile
     // element offset of (row r, first column of 16-byte unit u) in the v tile
     auto vt_off = [&](int r, int u) { return r * P + ((u ^ (((r / C::RP256) & C::SWZ_MASK) << 1)) << 3); };
 
@@ -618,8 +677,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const int idx = lane * C::CPL + u;
                 if (idx < LC) {
                     sgp->q2[idx] = (excl + loc[u]) * LOG2E;
-                    sgp->gw[idx] = cw[u];
-                    sgp->gr[idx] = cr[u];
+                    sgp->gw[idx] = cwb[u];
+                    sgp->gr[idx] = crb[u];
                 }
             }
             // same wave: its own LDS writes above are visible to these reads
@@ -666,7 +725,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
-            *reinterpret_cast<uint4*>(&sgp->V[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
+            *reinterpret_cast<uint4*>(&sgv[vt_off(tr, (int)(vcol0 >> 3))]) = rg.v[i];
         }
         if (wave == 0) stage_ctrl(rg.cd, rg.cw, rg.cr, n);
         if (next >= 0) load_chunk(rg, next);
@@ -689,7 +748,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     }
     auto load_vfrag = [&](int T, int nt) -> uint2 {
         const s16x4_t x =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sgp->V[vf_off[nt] + T * 16 * P]));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sgv[vf_off[nt] + T * 16 * P]));
         return __builtin_bit_cast(uint2, x);
     };
 
@@ -697,7 +756,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // wave*WCOLS + nt*16 + 4g) -> staged in the v tile in place: each wave
     // overwrites only its own columns of rows it has already read.
     auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) {
-        *reinterpret_cast<uint2*>(&sgp->V[ys_off[nt] + T * 16 * P]) =
+        *reinterpret_cast<uint2*>(&sgv[ys_off[nt] + T * 16 * P]) =
             make_uint2(pk_bf16(acc[0] * scale, acc[1] * scale), pk_bf16(acc[2] * scale, acc[3] * scale));
     };
 
@@ -767,7 +826,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sl = 4 * g + e;
-                    gv[e] = sl <= col ? exp2f(sgp->q2[T0 + sl] - qt) * sgp->gw[T0 + sl] * sm.psi[col - sl] : 0.f;
+                    gv[e] = sl <= col ? exp2f(sgp->q2[T0 + sl] - qt) * bf16_to_f32((uint16_t)sgp->gw[T0 + sl]) * sm.psi[col - sl] : 0.f;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -781,7 +840,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 }
                 const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
                                               make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
-                const float sc = sgp->gr[t];
+                const float sc = bf16_to_f32((uint16_t)sgp->gr[t]);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -799,7 +858,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     float val = 0.f;
                     if (jr < M && s <= T1) {
                         const float2 pw = sm.pw[T1 - s][jr < M ? jr : 0];
-                        val = ((col & 1) ? pw.y : pw.x) * exp2f(sgp->q2[s] - qe) * sgp->gw[s];
+                        val = ((col & 1) ? pw.y : pw.x) * exp2f(sgp->q2[s] - qe) * bf16_to_f32((uint16_t)sgp->gw[s]);
                     }
                     wv[e] = val;
                 }
@@ -968,7 +1027,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
             const int t = t0 + tr;
-            const uint4 outv = *reinterpret_cast<const uint4*>(&sgp->V[vt_off(tr, (int)(vcol0 >> 3))]);
+            const uint4 outv = *reinterpret_cast<const uint4*>(&sgv[vt_off(tr, (int)(vcol0 >> 3))]);
             if (tr < n) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
                 *reinterpret_cast<uint4*>(yg + off) = outv;
@@ -1104,7 +1163,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     f32x4_t st[NTW];
     float tr[4] = {1.f, 0.f, 1.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt];   // segment 0: from state_in; others: zero
+    for (int nt = 0; nt < NTW; ++nt) st[nt] = SEG ? f32x4_t{0.f, 0.f, 0.f, 0.f} : st_in[nt];
 
     ChunkRegs rb;
     if (SEG) {
@@ -1117,28 +1176,41 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             f32x4_t e[NTW];
             lookback(e);
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) st[nt] = st_in[nt] = e[nt];
+            for (int nt = 0; nt < NTW; ++nt) st[nt] = e[nt];
         }
-        wait_stores_complete();   // this wave's tile loads have landed
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            const int i = q * C::NW + wave;
-            if (i < nck) {
-                sgp = &stg[i];
-                stage_ctrl(ecd[q], ecw[q], ecr[q], min(LC, L - (c_begin + i) * LC));
-            }
-        }
-        __syncthreads();
-        // Sweep 1: the state through the segment from its entering state (zero,
-        // state_in for segment 0, the looked-back state for the last segment),
-        // recorded at every block start.
-        f32x4_t h0[C::RES][NBC][NTW];
+        // The control copies were issued before every tile copy: they have
+        // landed once at most this wave's tile copies are outstanding.  Wave w
+        // turns the controls of chunks w, w + NW, ... into the chunk factors.
+        wait_vmem_at_most<C::RES * TLW>();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < C::RES; ++i) {
+            if (i % C::NW == wave && i < nck) {
+                sgp = stage_c(i);
+                float cd[C::CPL];
+                uint32_t cw[C::CPL], cr[C::CPL];
+#pragma unroll
+                for (int u = 0; u < C::CPL; ++u) {
+                    const int idx = min(lane * C::CPL + u, LC - 1);
+                    cd[u] = sgp->q2[idx];
+                    cw[u] = sgp->gw[idx];
+                    cr[u] = sgp->gr[idx];
+                }
+                stage_ctrl(cd, cw, cr, min(LC, L - (c_begin + i) * LC));
+            }
+        }
+        // Sweep 1: the state through the segment from a zero entering state (the
+        // looked-back state for the last segment), recorded at every block
+        // start; each chunk as soon as its tile has landed.
+        f32x4_t h0[C::RES][NBC][NTW];
+        static_for<0, C::RES>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            wait_vmem_at_most<(C::RES - 1 - i) * TLW>();
+            lds_barrier();   // every wave's copies of tile i (and, first, the factors)
             if (i < nck) {
                 const int n = min(LC, L - (c_begin + i) * LC);
-                sgp = &stg[i];
+                sgp = stage_c(i);
+                sgv = stage_v(i);
 #pragma unroll
                 for (int Bi = 0; Bi < NBC; ++Bi) {
                     if (Bi * BLK < n) {
@@ -1153,34 +1225,39 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     }
                 }
             }
-        }
-        // Publish, look back.  gc: the entering state carried to the current
-        // block by the transfers of the blocks before it; the true state at a
-        // block start is h0 + gc (gc = 0 where sweep 1 began from the true state).
+        });
+        // Entering state, publish, look back.  gc: the entering state carried
+        // to the current block by the transfers of the blocks before it; the
+        // true state at a block start is h0 + gc (gc = 0 where sweep 1 began
+        // from the true state).
         f32x4_t gc[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) gc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (has_succ) {
-            if (seg == 0) {
-                publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
-            } else {
-                publish(plan.agg + (slot + seg) * (size_t)ROWS * P, st, FLAG_AGG, tr);
-                f32x4_t e[NTW];
-                lookback(e);
-                // inclusive = Lambda_seg * entering + aggregate
+        // st <- Lambda_seg * e + st (the inclusive state from the aggregate)
+        auto enter = [&](const f32x4_t (&e)[NTW]) {
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
+            for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const float ir = tr[i] * e[nt][i] - tr[i + 1] * e[nt][i + 1] + st[nt][i];
-                        const float ii = tr[i] * e[nt][i + 1] + tr[i + 1] * e[nt][i] + st[nt][i + 1];
-                        st[nt][i] = ir;
-                        st[nt][i + 1] = ii;
-                    }
-                    gc[nt] = e[nt];
+                for (int i = 0; i < 4; i += 2) {
+                    const float ir = tr[i] * e[nt][i] - tr[i + 1] * e[nt][i + 1] + st[nt][i];
+                    const float ii = tr[i] * e[nt][i + 1] + tr[i + 1] * e[nt][i] + st[nt][i + 1];
+                    st[nt][i] = ir;
+                    st[nt][i + 1] = ii;
                 }
-                publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
+                gc[nt] = e[nt];
             }
+        };
+        if (seg == 0) {
+            f32x4_t e[NTW];
+            load_entering(e);   // state_in, or zero
+            enter(e);
+            if (has_succ) publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
+        } else if (has_succ) {
+            publish(plan.agg + (slot + seg) * (size_t)ROWS * P, st, FLAG_AGG, tr);
+            f32x4_t e[NTW];
+            lookback(e);
+            enter(e);
+            publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
         }
         // Sweep 2: outputs from the resident chunks.  Each wave reads and
         // overwrites only its own columns, so no barrier is needed between chunks.
@@ -1190,7 +1267,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             if (i < nck) {
                 const int t0 = (c_begin + i) * LC;
                 const int n = min(LC, L - t0);
-                sgp = &stg[i];
+                sgp = stage_c(i);
+                sgv = stage_v(i);
 #pragma unroll
                 for (int Bi = 0; Bi < NBC; ++Bi) {
                     if (Bi * BLK < n) {
