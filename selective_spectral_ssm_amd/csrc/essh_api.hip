@@ -60,7 +60,7 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d) {
     if (check_dims(d, true) != ESSH_OK) return 0;
     const int lc = effective_lc(d);
     if (!chunked_supported(d->m, d->P, lc, d->io_dtype, d->ctrl_per_mode)) return 0;
-    return chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc);
+    return chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc, d->ctrl_per_mode);
 }
 
 essh_status essh_mixer_prefill(const essh_dims* d,
@@ -80,7 +80,7 @@ essh_status essh_mixer_prefill(const essh_dims* d,
 
     const int lc = effective_lc(d);
     const bool chunked = chunked_supported(d->m, d->P, lc, d->io_dtype, d->ctrl_per_mode);
-    const size_t need = chunked ? chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc) : 0;
+    const size_t need = chunked ? chunked_workspace_bytes(d->B, d->L, d->K_T, d->m, d->P, lc, d->ctrl_per_mode) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ESSH_ERR_WORKSPACE;
 
     if (d->B == 0) return ESSH_OK;
@@ -112,7 +112,7 @@ essh_status essh_mixer_prefill(const essh_dims* d,
     a.workspace_bytes = workspace_bytes;
     hipError_t e;
     if (chunked) {
-        ScanPlan plan = plan_chunked(d->B, d->L, d->K_T, d->m, d->P, lc);
+        ScanPlan plan = plan_chunked(d->B, d->L, d->K_T, d->m, d->P, lc, d->ctrl_per_mode);
         bind_workspace(plan, workspace, d->m, d->P);
         e = launch_prefill_chunked(a, d->m, d->P, plan, stream);
     } else {

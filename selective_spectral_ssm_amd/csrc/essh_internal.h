@@ -117,10 +117,12 @@ struct ScanPlan {
 // Launchers (host side).  Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_sequential(const PrefillArgs& a, int m, int P, int io_dtype, hipStream_t s);
 bool chunked_supported(int m, int P, int Lc, int io_dtype, int per_mode);
-ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc);
-size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc);
+ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode);
+size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc, int per_mode);
 void bind_workspace(ScanPlan& plan, void* workspace, int m, int P);
 hipError_t launch_prefill_chunked(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s);
+hipError_t launch_prefill_chunked_pm(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s);
+hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int B, int K, int K_T, int m, int P, hipStream_t s);

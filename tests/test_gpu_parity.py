@@ -99,12 +99,12 @@ def test_prefill_segment_scans(name, over, K_T):
 
 # Zero-lag correction (App. C.3, Eq. 24) on every prefill path: the look-back
 # and whole-sequence MFMA kernels (per-channel bf16), the three-launch scan,
-# and the sequential kernel (fp32 io, per-mode controls).
+# the sequential kernel (fp32 io) and the per-mode MFMA scan.
 ZERO_LAG = [("lookback_bf16", 1, dict(B=5, L=64 * 9 + 5, K=8), 8, 64),
             ("whole_seq_bf16", 1, dict(B=16, L=200, K=24), 24, 64),
             ("three_launch_bf16", 4, dict(L=1500), 6, 128),
             ("sequential_f32", 0, {}, 8, 0),
-            ("sequential_per_mode", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
+            ("per_mode_bf16", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
 
 
 @pytest.mark.parametrize("name,widx,over,K_T,Lc", ZERO_LAG, ids=[c[0] for c in ZERO_LAG])
@@ -136,6 +136,29 @@ def test_prefill_per_mode_controls():
         w = I.workload(widx, **over)
         inp = I.make_prefill_inputs(w, per_mode=True)
         check_prefill(f"per_mode_{inp['io']}", inp, w.K, 0)
+
+
+# Per-mode controls ([B, L, K, m], Eq. 5) on the MFMA scan: the three-launch
+# form (few sequences) and whole sequences, every chunk length, m = 1..8,
+# ragged tails, with the entering state and the zero-lag term.
+PER_MODE = [("pm_three_launch_m4", 1, dict(B=2, L=300, K=6), 6, 64),
+            ("pm_whole_seq_m4", 1, dict(B=16, L=150, K=24), 24, 64),
+            ("pm_m8_p128_lc32", 2, dict(B=1, L=161, K=4), 4, 32),
+            ("pm_m8_p128_lc128", 2, dict(B=2, L=333, K=3), 3, 128),
+            ("pm_m2_p32", 1, dict(B=2, L=97, K=3, m=2, P=32), 3, 64),
+            ("pm_m1_p16", 1, dict(B=3, L=75, K=2, m=1, P=16), 2, 64),
+            ("pm_dna_lc128", 4, dict(L=1000), 6, 128)]
+
+
+@pytest.mark.parametrize("name,widx,over,K_T,Lc", PER_MODE, ids=[c[0] for c in PER_MODE])
+def test_prefill_per_mode_chunked(name, widx, over, K_T, Lc):
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w, per_mode=True)
+    rng = np.random.default_rng(31)
+    s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    check_prefill(name, inp, K_T, Lc, state_in=s0)
+    zl = rng.uniform(0.0, 1.0, size=(w.K, w.m)).astype(np.float32)
+    check_prefill(name + "_zero_lag", inp, K_T, Lc, zl=zl)
 
 
 def test_prefill_chunk_length_invariance():
