@@ -34,7 +34,7 @@ SLEEP_CYCLES = 200_000_000
 # WRITE_SIZE passes scaled by the same counters on a plain copy of known size.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_chunk_mixer370m_kt24.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
-                  for f in ("prefill_chunk.hip", "essh_internal.h")]
+                  for f in ("prefill_chunk_kernel.h", "prefill_chunk.hip", "essh_internal.h")]
 METRIC = "selective spectral scan prefill tokens/s + decode µs/step, % of HBM roofline"
 
 
@@ -161,24 +161,26 @@ def time_launches(fn, steps, warmup):
 _CACHE = {}
 
 
-def workload_inputs(widx):
+def workload_inputs(widx, per_mode=False):
     from selective_spectral_ssm_amd import inputs as I
-    if widx not in _CACHE:
+    key = (widx, per_mode)
+    if key not in _CACHE:
         _CACHE.clear()
         w = I.workload(widx)
-        inp = I.make_prefill_inputs(w)
+        inp = I.make_prefill_inputs(w, per_mode=per_mode)
         d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
-        _CACHE[widx] = (w, inp, d)
-    return _CACHE[widx]
+        _CACHE[key] = (w, inp, d)
+    return _CACHE[key]
 
 
-def prefill_case(widx, K_T, steps, warmup):
+def prefill_case(widx, K_T, steps, warmup, per_mode=False):
+    """One workload at tier K_T; per_mode: clock and gates per mode ([B, L, K, m])."""
     from selective_spectral_ssm_amd import essh, sizes
-    w, inp, d = workload_inputs(widx)
+    w, inp, d = workload_inputs(widx, per_mode)
     call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
                         K_T=K_T, Lc=w.Lc, want_state=True)
     ms_step, ms_launch, ms_med = time_launches(call.run, steps, warmup)
-    nbytes = sizes.prefill_bytes(w.B, w.L, K_T, w.m, w.P, w.io, write_state=True)
+    nbytes = sizes.prefill_bytes(w.B, w.L, K_T, w.m, w.P, w.io, write_state=True, per_mode=per_mode)
     return dict(workload=w.name, K_T=K_T, ms_per_step=ms_step, us_per_launch=ms_launch * 1e3,
                 us_per_launch_median=ms_med * 1e3,
                 tokens_per_s=w.B * w.L / (ms_step * 1e-3),
@@ -344,6 +346,13 @@ def main():
                                                 "achieved_GBs")})
                 extra[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
         res["prefill_tiers"] = extra
+        pm = []
+        for widx, kt in ((1, 24), (2, 32), (2, 8)):
+            log(f"per-mode controls: workload {widx} K_T={kt}")
+            r, _, _ = prefill_case(widx, kt, max(10, args.steps // 4), 5, per_mode=True)
+            pm.append({k: r[k] for k in ("workload", "K_T", "us_per_launch", "kernel_tokens_per_s", "achieved_GBs")})
+            pm[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
+        res["prefill_per_mode"] = pm
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, w, 24)
