@@ -22,10 +22,10 @@
 // Re/Im(lambda_j^{15-s+T0}) are the same for every sub-block, so they are
 // built once per channel as MFMA operands held in registers; per sub-block
 // only v is scaled by b(s) and y by g_r(t) a(t).  Per 16 value columns that
-// is three v_mfma_f32_16x16x32_bf16:
+// is two v_mfma_f32_16x16x32_bf16:
 //   y^T = [b.v ; H_hi]^T [Psi^T ; C^T]         K = 16 positions + 16 state rows
-//   M   = [Lpow_hi Lpow_lo] [b.v ; b.v]        K = 16 positions x hi/lo, once for
-//                                              the bf16 hi and once for the lo part of b.v
+//   M   = [Lpow_hi Lpow_lo] [b.v ; b.v]        K = 16 positions x hi/lo of the
+//                                              lambda powers, b.v rounded to bf16 once
 // and h' = A_T (lambda^16 h + M) on the VALU.  b(s) grows within a sub-block;
 // a sub-block whose clock span could overflow it, and a ragged last one, take
 // an exact per-element path instead (same MFMA shapes, operands from exps).
@@ -60,7 +60,9 @@
 //   * v tiles are loaded with 16-byte loads one chunk ahead and stored to LDS
 //     row-major with an XOR swizzle of 16-byte units; the MFMA fragments (four
 //     consecutive positions of one column) come back with ds_read_b64_tr_b16.
-//     y is staged in place and written with 16-byte stores.
+//     y is staged in place and written with 16-byte stores.  The look-back
+//     launch's first sweep writes b(s) v(s) back over the fragment it read,
+//     and its output sweep reads those values instead of scaling v again.
 //   * Look-back messages are written and read with agent-scope atomic
 //     accesses (they bypass the per-XCD L2), flags carry a per-launch epoch,
 //     and every wait is bounded.
@@ -313,30 +315,45 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     unsigned tag = 0;
     if (SEG) {
         // Tickets are taken in the order workgroups start, so every predecessor
-        // of a segment (a smaller ticket) is already running or finished.
-        // Eight ticket counters, one per residue of blockIdx mod 8 (the XCD the
-        // hardware's round-robin dispatch sends the workgroup to), so that no
-        // single address takes every workgroup's atomic.  Counter x hands out
-        // the work items x, x + 8, x + 16, ... in start order.
+        // of a segment (a smaller ticket of the same counter) is already running
+        // or finished.  Eight ticket counters, one per residue of blockIdx mod 8
+        // (the XCD the hardware's round-robin dispatch sends the workgroup to),
+        // so that no single address takes every workgroup's atomic.
+        //   * nseq a multiple of 8: counter x owns the sequences
+        //     [x nseq/8, (x+1) nseq/8) and hands out their segments in
+        //     segment-major order, so one XCD reads all channels of those rows
+        //     and the clock and gate lines (channels innermost) are fetched by
+        //     one L2 only;
+        //   * otherwise counter x hands out the work items x, x + 8, x + 16, ...
+        // Either way a segment's predecessor comes from the same counter
+        // earlier, or (second form) from a smaller global ticket.
         const int xq = (int)(blockIdx.x & 7u);
         if (tid == 0) {
             const unsigned ep = ld_agent_u(&plan.hdr[SCAN_HDR_EPOCH]);
             const unsigned t = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_TICKET0 + SCAN_HDR_STRIDE * xq], 1u,
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sm.ticket = (int)(t * 8u + (unsigned)xq);
+            sm.ticket = (int)t;
             sm.epoch = ep;
         }
         __syncthreads();
-        const int ticket = sm.ticket;
+        const int tloc = sm.ticket;
         tag = ((sm.epoch + 1u) & 0x3FFFFFFFu) << 2;
-        if (ticket >= plan.nblocks) {
+        const bool xcd_rows = (plan.nseq & 7) == 0;
+        const int nsx = plan.nseq >> 3;
+        const int ticket = xcd_rows ? tloc : tloc * 8 + xq;
+        if (ticket >= (xcd_rows ? plan.nblocks >> 3 : plan.nblocks)) {
             // Only possible with a workspace that was not zero-filled before first use.
             if (tid == 0) __hip_atomic_fetch_or(&plan.hdr[SCAN_HDR_ERROR], SCAN_ERR_TICKET, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
-        seg = ticket / plan.nseq;
-        seq = ticket - seg * plan.nseq;
+        if (xcd_rows) {
+            seg = tloc / nsx;
+            seq = xq * nsx + (tloc - seg * nsx);
+        } else {
+            seg = ticket / plan.nseq;
+            seq = ticket - seg * plan.nseq;
+        }
     } else {
         // segment-major order: neighbouring work items are neighbouring channels
         // of one batch row over the same positions
@@ -847,6 +864,20 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             make_uint2(pk_bf16(acc[0] * scale, acc[1] * scale), pk_bf16(acc[2] * scale, acc[3] * scale));
     };
 
+    // b(s) v(s) of fragment (T, nt) kept for a later sweep, in place: the
+    // fragment's footprint in the tile (rows T0..T0+15, the tile's 16 columns)
+    // is 64 slots of 8 bytes, and lane l takes row T0 + l/4, 16-byte unit
+    // (l/2)%2 of the tile's two, half l%2.  Only the wave that read the
+    // fragment writes its slots, after reading it.
+    int bw_off[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+        bw_off[nt] = vt_off(lane >> 2, ((wave * WCOLS + nt * 16) >> 3) + ((lane >> 1) & 1)) + (lane & 1) * 4;
+    auto store_bv = [&](int T, int nt, uint2 x) { *reinterpret_cast<uint2*>(&sgv[bw_off[nt] + T * 16 * P]) = x; };
+    auto load_bv = [&](int T, int nt) -> uint2 {
+        return *reinterpret_cast<const uint2*>(&sgv[bw_off[nt] + T * 16 * P]);
+    };
+
     auto hi4 = [&](const f32x4_t& x) -> uint2 { return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])); };
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
@@ -861,19 +892,15 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         float lam[4];   // Lambda_T for modes 2g, 2g+1
         if (bk.y == 0.f) {
             // factored path: scale v by b(s), constant operands.  b(s) v(s) is
-            // split into bf16 hi + lo: the output product uses hi, the state
-            // product both, so the state keeps ~16 mantissa bits.
+            // rounded to bf16 once and feeds both products; the state operand
+            // carries its hi and lo halves, so the state product is exact up to
+            // that one rounding of b(s) v(s).
             const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
-            uint2 bv[NTW], bl[NTW];
+            uint2 bv[NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const float x0 = b4.x * lo_f32(vfr[nt].x), x1 = b4.y * hi_f32(vfr[nt].x);
-                const float x2 = b4.z * lo_f32(vfr[nt].y), x3 = b4.w * hi_f32(vfr[nt].y);
-                const uint32_t h01 = pk_bf16(x0, x1), h23 = pk_bf16(x2, x3);
-                bv[nt] = make_uint2(h01, h23);
-                bl[nt] = make_uint2(pk_bf16(x0 - lo_f32(h01), x1 - hi_f32(h01)),
-                                    pk_bf16(x2 - lo_f32(h23), x3 - hi_f32(h23)));
-            }
+            for (int nt = 0; nt < NTW; ++nt)
+                bv[nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr[nt].x), b4.y * hi_f32(vfr[nt].x)),
+                                    pk_bf16(b4.z * lo_f32(vfr[nt].y), b4.w * hi_f32(vfr[nt].y)));
             if (out) {
                 const float sc = sgp->ag[T0 + col];
 #pragma unroll
@@ -886,9 +913,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const float at = bk.x;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
-                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bl[nt], bl[nt]), mv, 0, 0, 0);
+                const f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
+                                                                          f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
                     const float lr = l16[i], li = l16[i + 1];
@@ -1075,9 +1101,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     //   h'   = Lambda_e lambda^BLK h + A_e sum_s lambda^{BLK-1-s} b(s) v(s)
     // (positions relative to the block, H_s = a at the block's entry, A_e = a at
     // its end, Lambda_e = e^{-clock span}).  The state is carried once per block;
-    // per sub-block only b(s) v(s) is formed (bf16 hi + lo) and fed to the
+    // per sub-block only b(s) v(s) is formed (rounded to bf16) and fed to the
     // constant-operand products.
-    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, float (&tr)[4]) {
+    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb, float (&tr)[4]) {
         const float4 bk = sgp->blkB[Bi];
         uint2 hh[NTW];
         if (out) {
@@ -1098,15 +1124,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 const uint2 vfr = load_vfrag(T, nt);
-                const float x0 = b4.x * lo_f32(vfr.x), x1 = b4.y * hi_f32(vfr.x);
-                const float x2 = b4.z * lo_f32(vfr.y), x3 = b4.w * hi_f32(vfr.y);
-                const uint32_t h01 = pk_bf16(x0, x1), h23 = pk_bf16(x2, x3);
-                bvh[aa][nt] = make_uint2(h01, h23);
-                const uint2 bl = make_uint2(pk_bf16(x0 - lo_f32(h01), x1 - hi_f32(h01)),
-                                            pk_bf16(x2 - lo_f32(h23), x3 - hi_f32(h23)));
+                bvh[aa][nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr.x), b4.y * hi_f32(vfr.x)),
+                                         pk_bf16(b4.z * lo_f32(vfr.y), b4.w * hi_f32(vfr.y)));
+                if (wb) store_bv(T, nt, bvh[aa][nt]);
                 mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bvh[aa][nt], bvh[aa][nt]), mv[nt],
                                                                  0, 0, 0);
-                mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bl, bl), mv[nt], 0, 0, 0);
             }
             if (out) {
                 const float sc = sgp->ag[T0 + col];
@@ -1147,7 +1169,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 
     // Outputs of one whole block on the block path from the true state h
     // entering it; the state itself is not carried (the look-back launch's
-    // output sweep knows every block's entering state).
+    // output sweep knows every block's entering state).  The b(s) v(s)
+    // fragments are the ones the first sweep wrote back into the tile.
     auto block_out = [&](const f32x4_t (&h)[NTW], int Bi) {
         const float4 bk = sgp->blkB[Bi];
         uint2 hh[NTW];
@@ -1159,13 +1182,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int aa = 0; aa < NB; ++aa) {
             const int T = Bi * NB + aa, T0 = T * 16;
-            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const uint2 vfr = load_vfrag(T, nt);
-                bvh[aa][nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr.x), b4.y * hi_f32(vfr.x)),
-                                         pk_bf16(b4.z * lo_f32(vfr.y), b4.w * hi_f32(vfr.y)));
-            }
+            for (int nt = 0; nt < NTW; ++nt) bvh[aa][nt] = load_bv(T, nt);
             const float sc = sgp->ag[T0 + col];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
@@ -1188,7 +1206,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) {
         for (int Bi = 0; Bi * BLK < n; ++Bi) {
             if (sgp->blkB[Bi].w == 0.f) {
-                block_fast(st, Bi, out, tr);
+                block_fast(st, Bi, out, false, tr);
             } else {
                 const int tend = min(n, (Bi + 1) * BLK);
                 for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, out, tr, lpA[NB - 1], l16);
@@ -1392,7 +1410,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
                         for (int nt = 0; nt < NTW; ++nt) h0[i][Bi][nt] = st[nt];
                         if (sgp->blkB[Bi].w == 0.f) {
-                            block_fast(st, Bi, false, tr);
+                            block_fast(st, Bi, false, true, tr);
                         } else {
                             const int tend = min(n, (Bi + 1) * BLK);
                             for (int T = Bi * NB; T * 16 < tend; ++T) subblock(st, T, n, false, tr, lpA[NB - 1], l16);

@@ -382,7 +382,9 @@ def test_decode_iterated_equals_prefill():
     assert block_err(to_host_f64(y_dec), y_ref, 2) <= TOL["bf16"]
     assert block_err(to_host_f64(st[0]), s_ref, 1) <= 1e-5     # fp32 recurrence on both sides
     assert block_err(to_host_f64(y_dec), to_host_f64(y_pf), 2) <= TOL["bf16"]
-    assert block_err(to_host_f64(s_pf), to_host_f64(st[0]), 1) <= 1e-3
+    # the chunked scan rounds b(s) v(s) to bf16 once before its state product, so
+    # its state meets the bf16-io bound, not the fp32 one of the decode recurrence
+    assert block_err(to_host_f64(s_pf), to_host_f64(st[0]), 1) <= TOL["bf16"]
 
 
 def test_decode_after_prefill_full_shape_sampled():
