@@ -57,9 +57,11 @@
 //     state lives in VGPRs in the 16x16 MFMA accumulator layout (lane (g,col)
 //     holds state rows 4g..4g+3 = (mode 2g, re/im), (mode 2g+1, re/im) of
 //     column col).  Every product of one accumulation chain has one MFMA shape.
-//   * v tiles are loaded with 16-byte loads one chunk ahead and stored to LDS
-//     row-major with an XOR swizzle of 16-byte units; the MFMA fragments (four
-//     consecutive positions of one column) come back with ds_read_b64_tr_b16.
+//   * v tiles are loaded with 16-byte loads one chunk ahead (streaming) or
+//     copied global-to-LDS up front (look-back) into LDS blocked by 16-column
+//     tiles, [P/16][Lc][16], so that one wave's columns are contiguous runs;
+//     the MFMA fragments (four consecutive positions of one column) come back
+//     with ds_read_b64_tr_b16.
 //     y is staged in place and written with 16-byte stores.  The look-back
 //     launch's first sweep writes b(s) v(s) back over the fragment it read,
 //     and its output sweep reads those values instead of scaling v again.
@@ -114,7 +116,6 @@ constexpr int stage_bytes(int P, int LC) {
 constexpr int resident_chunks(int P, int LC) {
     return 40960 / stage_bytes(P, LC) < 1 ? 1 : (40960 / stage_bytes(P, LC) > 4 ? 4 : 40960 / stage_bytes(P, LC));
 }
-
 namespace {
 
 template <int P_, int M_, int LC_>
@@ -134,11 +135,11 @@ struct Cfg {
     static constexpr int RPI = 64 / LPR;            // v rows per wave load
     static constexpr int NLD = LC / RPI;            // wave loads per chunk
     static constexpr int CPL = (LC + 63) / 64;     // control positions per lane of wave 0
-    // v tile rows are P bf16 = P/8 16-byte units; unit u of row r is stored at
-    // unit u ^ swz(r), swz(r) = 2 * ((r / RP256) % (P/16)), which spreads the
-    // 16 rows a transposing fragment read touches over all LDS banks.
-    static constexpr int RP256 = P >= 128 ? 1 : 128 / P;   // rows per 256 bytes
-    static constexpr int SWZ_MASK = P / 16 - 1;
+    // v tile in LDS: blocked by 16-column tiles, [P/16][LC][16] bf16, so that
+    // the 16 rows of one tile form 512 contiguous bytes (a transposing
+    // fragment read, and every copy or read of one wave's columns, is one
+    // contiguous run).
+    static constexpr int TBLK = LC * 16;            // elements of one 16-column tile block
     // chunks of a segment kept resident in LDS between the two sweeps
     static constexpr int RES = resident_chunks(P, LC);
     static_assert(P % 16 == 0 && NT % NW == 0, "P must be 16, 32, 64 or 128");
@@ -173,7 +174,7 @@ struct __align__(16) StagePM {
     float gr[C::M][C::LC];
 };
 
-// v tile of a staged chunk: [t][P] bf16 (swizzled units); y is staged in place.
+// v tile of a staged chunk: [P/16][LC][16] bf16; y is staged in place.
 template <class C>
 struct __align__(16) VTile {
     uint16_t V[C::LC * C::P];
@@ -301,8 +302,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     __shared__ Stage<C> sc0, sc1, sc2, sc3;
     __shared__ VTile<C> sv0, sv1, sv2, sv3;
     __shared__ StagePM<C> spm;   // per-mode launches only
-    auto stage_c = [&](int i) -> Stage<C>* { return i == 0 ? &sc0 : i == 1 ? &sc1 : i == 2 ? &sc2 : &sc3; };
-    auto stage_v = [&](int i) -> uint16_t* { return i == 0 ? sv0.V : i == 1 ? sv1.V : i == 2 ? sv2.V : sv3.V; };
+    auto stage_c = [&](int i) __attribute__((always_inline)) -> Stage<C>* {
+        return i == 0 ? &sc0 : i == 1 ? &sc1 : i == 2 ? &sc2 : &sc3;
+    };
+    auto stage_v = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+        return i == 0 ? sv0.V : i == 1 ? sv1.V : i == 2 ? sv2.V : sv3.V;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -398,21 +403,60 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     }
 
+    // ---- state in the accumulator layout ---------------------------------------------
+    // The entering state.  Segment 0 reads state_in before any segment of the
+    // sequence can finish (a look-back segment before it publishes its
+    // inclusive state, which the last segment waits for), so that an aliasing
+    // state_out written by the last segment cannot race with it.  In the
+    // three-launch scan the aggregate launch copies state_in into the
+    // entering-state slot of segment 0 and the streaming launch reads only
+    // those slots.  The look-back launch reads it after its first sweep, so
+    // that no register load is outstanding while its tile copies land.
+    const bool split_stream = (MODE == MODE_STREAM || MODE == MODE_STREAM_PM) && nseg > 1;
+    auto load_entering = [&](f32x4_t (&x)[NTW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = wave * WCOLS + nt * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i, j = row >> 1, cmp = row & 1;
+                float v = 0.f;
+                if (split_stream) {
+                    if (row < ROWS) v = plan.incl[((slot + seg) * ROWS + row) * (size_t)P + p];
+                } else if (seg == 0 && a.state_in && j < M) {
+                    v = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
+                }
+                x[nt][i] = v;
+            }
+        }
+    };
+    // The streaming launches issue these loads before building the tables, so
+    // that the tables' work covers their latency.
+    f32x4_t st_in[NTW];
+    if (!SEG) load_entering(st_in);
+
     // ---- segmented scan: every chunk of the segment is requested at once -------------------
     // Asynchronous global-to-LDS copies only (no register loads): first the
     // controls of every resident chunk (clock into q2, gate bits into gw/gr;
     // 64 positions per wave instruction, spread over the waves), then the v
-    // tiles (16 bytes per lane; a wave instruction fills 1 KB of the tile, so
-    // each lane fetches the 16-byte unit whose swizzled slot is lane-th of that
-    // block).  Every wave issues the same number of tile copies per chunk, TLW,
+    // tiles of the wave's own columns.  Every wave issues the same number of
+    // tile copies per chunk, TLW,
     // after all control copies, so "chunk i has landed" is "at most
     // (RES-1-i) * TLW copies outstanding" in every wave.  Rows past the
     // segment or past L repeat a valid row; their values only reach positions
     // that are never written.
-    constexpr int UPR = P / 8;                 // 16-byte units per tile row
-    constexpr int INSTR = LC * UPR / 64;       // wave instructions per tile
-    static_assert(INSTR % C::NW == 0, "tile instructions must divide over the waves");
-    constexpr int TLW = INSTR / C::NW;         // tile copies per wave and chunk
+    // A wave's tile copy fills 1 KB of LDS, 32 rows of one 16-column tile
+    // block (lane l: row l/2, 8-column half l%2); each wave copies the tiles of
+    // its own columns, TLW instructions per chunk.
+    constexpr int TLW = NTW * (LC / 32);       // tile copies per wave and chunk
+    // one tile copy of local chunk position row base `tb` (first position of the
+    // chunk) into the tile block array `dst`; rows at or past `tend` repeat row tend-1
+    auto copy_tile = [&](uint16_t* dst, int it, int tb, int tend) __attribute__((always_inline)) {
+        const int j = wave * NTW + it / (LC / 32), q = it % (LC / 32);
+        const int t = min(tb + 32 * q + (lane >> 1), tend - 1);
+        const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + j * 16 + (lane & 1) * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + j * C::TBLK + q * 512), 16, 0, 0);
+    };
     if (SEG) {
         constexpr int CIA = (LC + 63) / 64;    // instructions per control array of a chunk
         constexpr int NCI = C::RES * 3 * CIA;
@@ -435,15 +479,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int i = 0; i < C::RES; ++i) {
 #pragma unroll
-            for (int it = 0; it < INSTR / C::NW; ++it) {
-                const int ins = it * C::NW + wave;
-                const int sl = ins * 64 + lane;
-                const int r = sl / UPR, pu = sl - r * UPR;
-                const int u = pu ^ (((r / C::RP256) & C::SWZ_MASK) << 1);
-                const int t = min((c_begin + i) * LC + r, L - 1);   // rows past L: any valid row
-                const uint16_t* src = vg + (((size_t)b * L + t) * K + k) * P + u * 8;
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_v(i) + ins * 512), 16, 0, 0);
-            }
+            for (int it = 0; it < TLW; ++it)   // rows past L: any valid row
+                copy_tile(stage_v(i), it, (c_begin + i) * LC, L);
         }
     }
 
@@ -516,7 +553,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // its aggregate sweep and the output operands in its output sweep only.
     bf16x8_t yD[NB], yB12, yB3, lpA[NB];
     float lB[4], l16[4];
-    auto make_out_constants = [&]() {
+    auto make_out_constants = [&]() __attribute__((always_inline)) {
         u16x8_t h;
 #pragma unroll
         for (int aa = 0; aa < NB; ++aa) {
@@ -550,7 +587,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
         yB3 = to_bf16x8(h);
     };
-    auto make_state_constants = [&]() {
+    auto make_state_constants = [&]() __attribute__((always_inline)) {
         u16x8_t h;
         const int jr = col >> 1;
 #pragma unroll
@@ -582,7 +619,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
     // The sub-block path's state operand (lpA[NB-1]) and lambda^16, rebuilt
     // from the tables where the state operands are no longer held.
-    auto make_sub_al = [&]() -> bf16x8_t {
+    auto make_sub_al = [&]() __attribute__((always_inline)) -> bf16x8_t {
         u16x8_t h;
         const int jr = col >> 1;
 #pragma unroll
@@ -598,7 +635,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
         return to_bf16x8(h);
     };
-    auto make_l16 = [&](float (&o)[4]) {
+    auto make_l16 = [&](float (&o)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * g + hh;
@@ -610,36 +647,6 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     make_state_constants();
     if (!SEG) make_out_constants();
 
-    // ---- state in the accumulator layout ---------------------------------------------
-    // The entering state.  Segment 0 reads state_in before any segment of the
-    // sequence can finish (a look-back segment before it publishes its
-    // inclusive state, which the last segment waits for), so that an aliasing
-    // state_out written by the last segment cannot race with it.  In the
-    // three-launch scan the aggregate launch copies state_in into the
-    // entering-state slot of segment 0 and the streaming launch reads only
-    // those slots.  The look-back launch reads it after its first sweep, so
-    // that no register load is outstanding while its tile copies land.
-    const bool split_stream = (MODE == MODE_STREAM || MODE == MODE_STREAM_PM) && nseg > 1;
-    auto load_entering = [&](f32x4_t (&x)[NTW]) {
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const int p = wave * WCOLS + nt * 16 + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i, j = row >> 1, cmp = row & 1;
-                float v = 0.f;
-                if (split_stream) {
-                    if (row < ROWS) v = plan.incl[((slot + seg) * ROWS + row) * (size_t)P + p];
-                } else if (seg == 0 && a.state_in && j < M) {
-                    v = a.state_in[((((size_t)b * K + k) * M + j) * 2 + cmp) * P + p];
-                }
-                x[nt][i] = v;
-            }
-        }
-    };
-    f32x4_t st_in[NTW];
-    if (!SEG) load_entering(st_in);
-
     // ---- chunk pipeline helpers ---------------------------------------------------------
     const int vrow_l = lane / C::LPR;          // row of this lane inside a wave load
     const int vunit = lane % C::LPR;           // 16-byte unit of this lane inside a row
@@ -647,7 +654,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     Stage<C>* sgp = stage_c(0);   // staged chunk the helpers work on: factors
     uint16_t* sgv = stage_v(0);   // ... and v tile
     // element offset of (row r, first column of 16-byte unit u) in the v tile
-    auto vt_off = [&](int r, int u) { return r * P + ((u ^ (((r / C::RP256) & C::SWZ_MASK) << 1)) << 3); };
+    auto vt_off = [&](int r, int u) __attribute__((always_inline)) { return (u >> 1) * C::TBLK + r * 16 + ((u & 1) << 3); };
 
     // Loads of one chunk held in registers until they are staged into LDS.
     // per-mode controls of a chunk spread over every thread: LC * M values each
@@ -660,7 +667,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         uint32_t mw[PMC], mr[PMC];                  // element tid + u * THREADS = position * M + mode
     };
 
-    auto load_chunk = [&](ChunkRegs& rg, int c) {
+    auto load_chunk = [&](ChunkRegs& rg, int c) __attribute__((always_inline)) {
         const int t0 = c * LC;
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
@@ -711,7 +718,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // One wave: clock sums and per-position factors of the staged chunk (n
     // valid positions) from the controls it holds.
     auto stage_ctrl = [&](const float (&cd)[C::CPL], const uint32_t (&cwb)[C::CPL], const uint32_t (&crb)[C::CPL],
-                          int n) {
+                          int n) __attribute__((always_inline)) {
         {
             float cw[C::CPL], cr[C::CPL];
 #pragma unroll
@@ -781,7 +788,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // Register path: v tile and controls of the loaded chunk -> LDS, then the
     // loads of chunk `next` (if >= 0) are issued so that they overlap this
     // chunk's arithmetic.  Starts and ends with a barrier.
-    auto stage_chunk = [&](ChunkRegs& rg, int n, int next) {
+    auto stage_chunk = [&](ChunkRegs& rg, int n, int next) __attribute__((always_inline)) {
         __syncthreads();   // previous readers of the staged chunk are done
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
@@ -841,7 +848,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // of 16 lanes, ds_read_b64_tr_b16 returns to lane i, element e, the (i%4)-th
     // 16-bit value at the address of lane 4e + i/4; so lane (g, col) supplies
     // the address of row T0 + 4g + col/4, columns 4*(col%4) .. +3 of the tile.
-    // The swizzle repeats every 8 rows, so sub-block T is 16*T rows further.
+    // Sub-block T is 16 rows = 256 elements further in the tile block.
     int vf_off[NTW], ys_off[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
@@ -850,40 +857,39 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         const int p1 = wave * WCOLS + nt * 16 + 4 * g;
         ys_off[nt] = vt_off(col, p1 >> 3) + (p1 & 7);
     }
-    auto load_vfrag = [&](int T, int nt) -> uint2 {
+    auto load_vfrag = [&](int T, int nt) __attribute__((always_inline)) -> uint2 {
         const s16x4_t x =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sgv[vf_off[nt] + T * 16 * P]));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&sgv[vf_off[nt] + T * 256]));
         return __builtin_bit_cast(uint2, x);
     };
 
     // y tile of sub-block T (lane holds y(t = T0+col, p1 + i), i < 4, p1 =
     // wave*WCOLS + nt*16 + 4g) -> staged in the v tile in place: each wave
     // overwrites only its own columns of rows it has already read.
-    auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) {
-        *reinterpret_cast<uint2*>(&sgv[ys_off[nt] + T * 16 * P]) =
+    auto stage_y = [&](int T, int nt, const f32x4_t& acc, float scale) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(&sgv[ys_off[nt] + T * 256]) =
             make_uint2(pk_bf16(acc[0] * scale, acc[1] * scale), pk_bf16(acc[2] * scale, acc[3] * scale));
     };
 
     // b(s) v(s) of fragment (T, nt) kept for a later sweep, in place: the
-    // fragment's footprint in the tile (rows T0..T0+15, the tile's 16 columns)
-    // is 64 slots of 8 bytes, and lane l takes row T0 + l/4, 16-byte unit
-    // (l/2)%2 of the tile's two, half l%2.  Only the wave that read the
-    // fragment writes its slots, after reading it.
+    // fragment's footprint in the tile (rows T0..T0+15 of one 16-column tile
+    // block) is 512 contiguous bytes, and lane l takes the l-th 8 bytes.  Only
+    // the wave that read the fragment writes its slots, after reading it.
     int bw_off[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-        bw_off[nt] = vt_off(lane >> 2, ((wave * WCOLS + nt * 16) >> 3) + ((lane >> 1) & 1)) + (lane & 1) * 4;
-    auto store_bv = [&](int T, int nt, uint2 x) { *reinterpret_cast<uint2*>(&sgv[bw_off[nt] + T * 16 * P]) = x; };
-    auto load_bv = [&](int T, int nt) -> uint2 {
-        return *reinterpret_cast<const uint2*>(&sgv[bw_off[nt] + T * 16 * P]);
+        bw_off[nt] = (wave * NTW + nt) * C::TBLK + lane * 4;
+    auto store_bv = [&](int T, int nt, uint2 x) __attribute__((always_inline)) { *reinterpret_cast<uint2*>(&sgv[bw_off[nt] + T * 256]) = x; };
+    auto load_bv = [&](int T, int nt) __attribute__((always_inline)) -> uint2 {
+        return *reinterpret_cast<const uint2*>(&sgv[bw_off[nt] + T * 256]);
     };
 
-    auto hi4 = [&](const f32x4_t& x) -> uint2 { return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])); };
+    auto hi4 = [&](const f32x4_t& x) __attribute__((always_inline)) -> uint2 { return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])); };
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
     auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4], const bf16x8_t& al,
-                        const float (&l16)[4]) {
+                        const float (&l16)[4]) __attribute__((always_inline)) {
         const int T0 = T * 16;
         const float2 bk = sgp->blk[T];
         uint2 vfr[NTW];
@@ -1103,7 +1109,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // its end, Lambda_e = e^{-clock span}).  The state is carried once per block;
     // per sub-block only b(s) v(s) is formed (rounded to bf16) and fed to the
     // constant-operand products.
-    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb, float (&tr)[4]) {
+    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb, float (&tr)[4]) __attribute__((always_inline)) {
         const float4 bk = sgp->blkB[Bi];
         uint2 hh[NTW];
         if (out) {
@@ -1171,7 +1177,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // entering it; the state itself is not carried (the look-back launch's
     // output sweep knows every block's entering state).  The b(s) v(s)
     // fragments are the ones the first sweep wrote back into the tile.
-    auto block_out = [&](const f32x4_t (&h)[NTW], int Bi) {
+    auto block_out = [&](const f32x4_t (&h)[NTW], int Bi) __attribute__((always_inline)) {
         const float4 bk = sgp->blkB[Bi];
         uint2 hh[NTW];
 #pragma unroll
@@ -1203,7 +1209,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 
     // All positions of the staged chunk (n valid): whole blocks on the block
     // path, the others (ragged, or a clock span too large) sub-block by sub-block.
-    auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) {
+    auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) __attribute__((always_inline)) {
         for (int Bi = 0; Bi * BLK < n; ++Bi) {
             if (sgp->blkB[Bi].w == 0.f) {
                 block_fast(st, Bi, out, false, tr);
@@ -1215,7 +1221,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
 
     // staged y -> global, 16 bytes per lane (the units this lane loaded v from)
-    auto store_y = [&](int t0, int n) {
+    auto store_y = [&](int t0, int n) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int tr = i * C::RPI + vrow_l;
@@ -1229,7 +1235,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
 
     // Look-back message rows: rows (j, re/im) of this lane's value columns.
-    auto publish = [&](float* dst, const f32x4_t (&s)[NTW], unsigned kind, const float (&trn)[4]) {
+    auto publish = [&](float* dst, const f32x4_t (&s)[NTW], unsigned kind, const float (&trn)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int p = wave * WCOLS + nt * 16 + col;
@@ -1260,7 +1266,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // 0 polls the flags of up to 64 predecessors at once; once every
     // predecessor nearer than the nearest inclusive one has its aggregate out,
     // all of those messages are read (independent loads) and folded in order.
-    auto lookback = [&](f32x4_t (&e)[NTW]) {
+    auto lookback = [&](f32x4_t (&e)[NTW]) __attribute__((always_inline)) {
         float cf[4] = {1.f, 0.f, 1.f, 0.f};   // accumulated transfer of modes 2g, 2g+1
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) e[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1396,7 +1402,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         // looked-back state for the last segment), recorded at every block
         // start; each chunk as soon as its tile has landed.
         f32x4_t h0[C::RES][NBC][NTW];
-        static_for<0, C::RES>([&](auto ic) {
+        static_for<0, C::RES>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             wait_vmem_at_most<(C::RES - 1 - i) * TLW>();
             lds_barrier();   // every wave's copies of tile i (and, first, the factors)
@@ -1427,7 +1433,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) gc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         // st <- Lambda_seg * e + st (the inclusive state from the aggregate)
-        auto enter = [&](const f32x4_t (&e)[NTW]) {
+        auto enter = [&](const f32x4_t (&e)[NTW]) __attribute__((always_inline)) {
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
