@@ -81,6 +81,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // Read-only fp32 data addressed uniformly across a workgroup (constant address space).
 typedef const __attribute__((address_space(4))) float* cfloat_p;
@@ -1220,7 +1221,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     };
 
-    // staged y -> global, 16 bytes per lane (the units this lane loaded v from)
+    // staged y -> global, 16 bytes per lane (the units this lane loaded v from).
+    // A streaming launch with P >= 128 (64 bytes of a row per wave) stores
+    // non-temporally: measured faster there, slower with narrower rows.
     auto store_y = [&](int t0, int n) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
@@ -1229,7 +1232,32 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const uint4 outv = *reinterpret_cast<const uint4*>(&sgv[vt_off(tr, (int)(vcol0 >> 3))]);
             if (tr < n) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
-                *reinterpret_cast<uint4*>(yg + off) = outv;
+                if constexpr (P >= 128 && MODE == MODE_STREAM)
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, outv), reinterpret_cast<u32x4_t*>(yg + off));
+                else
+                    *reinterpret_cast<uint4*>(yg + off) = outv;
+            }
+        }
+    };
+
+    // staged y -> global by whole rows, non-temporally: each 128-byte line is
+    // written by one instruction, so none is left dirty in L2 when the kernel
+    // ends.  Needs every wave's y of the chunk staged (a barrier before).  Used
+    // by the look-back launch with P <= 64 (measured faster there; with wider
+    // rows the read-back crosses too many tile blocks).
+    auto store_y_rows = [&](int t0, int n) __attribute__((always_inline)) {
+        constexpr int UPR = P / 8;                     // 16-byte units per row
+        constexpr int RPW = 64 / UPR;                  // rows per wave instruction
+        constexpr int NI = LC / (RPW * C::NW);         // instructions per wave
+        static_assert(LC % (RPW * C::NW) == 0, "rows must divide over the waves");
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = (i * C::NW + wave) * RPW + lane / UPR;
+            const int u = lane % UPR;
+            const uint4 outv = *reinterpret_cast<const uint4*>(&sgv[vt_off(r, u)]);
+            if (r < n) {
+                const size_t off = (((size_t)b * L + t0 + r) * K + k) * P + u * 8;
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, outv), reinterpret_cast<u32x4_t*>(yg + off));
             }
         }
     };
@@ -1459,7 +1487,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             publish(plan.incl + (slot + seg) * (size_t)ROWS * P, st, FLAG_INCL, tr);
         }
         // Sweep 2: outputs from the resident chunks.  Each wave reads and
-        // overwrites only its own columns, so no barrier is needed between chunks.
+        // overwrites only its own columns; a barrier per chunk precedes the
+        // whole-row stores.
         make_out_constants();
 #pragma unroll
         for (int i = 0; i < C::RES; ++i) {
@@ -1497,7 +1526,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                         }
                     }
                 }
-                store_y(t0, n);
+                if constexpr (P <= 64) {
+                    lds_barrier();   // every wave's y of this chunk is staged
+                    store_y_rows(t0, n);
+                } else {
+                    store_y(t0, n);
+                }
             }
         }
     } else {
