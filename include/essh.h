@@ -158,6 +158,9 @@ essh_status essh_mixer_prefill(const essh_dims* d,
  *   zl                   [n_layers, K, m] fp32 zero-lag coefficients, or NULL
  *   state                [n_layers, B, K, m, 2, P] fp32, updated in place (k < K_T only)
  *   y                    [n_layers, B, K, P] io dtype; channels k >= K_T untouched
+ *
+ * Returns ESSH_ERR_UNSUPPORTED when B or n_layers exceeds 65535 (one launch
+ * covers layers x batch rows as grid extents) or n_layers * B * K * P exceeds 2^30.
  */
 essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
                                    const void* v, const float* delta, const void* g_w, const void* g_r,

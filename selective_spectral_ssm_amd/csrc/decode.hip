@@ -10,29 +10,29 @@
 // the state back and writes y.  Consecutive lanes are consecutive p, so every
 // state plane, v and y access of a wave is one contiguous run.
 //
-// The pole rotations rho(cos theta, sin theta) are per (layer, k, j) and
-// shared by the P lanes of a channel: the first m lanes of each channel group
-// in a wave evaluate one each and the wave broadcasts them with cross-lane
-// reads, instead of every lane evaluating m sin/cos pairs.
+// The grid is (channel groups, batch rows, layers): a workgroup holds
+// max(P, 64) lanes, i.e. 64/P channels of one (layer, b) when P < 64 and one
+// channel otherwise, so no lane divides to find its indices.  Every global
+// load of a lane is issued first; the pole rotations
+// rho (cos theta, sin theta), per (layer, k, j) and shared by the P lanes of a
+// channel, are evaluated while those loads are in flight, by the first m lanes
+// of each channel group in a wave, and broadcast with cross-lane reads.
 #include "essh_internal.h"
 
 namespace essh {
 namespace {
 
 template <int M, typename IO, bool PER_MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(128)
 decode_kernel(DecodeArgs a, int P) {
     using io = io_traits<IO>;
-    const long long total = (long long)a.n_layers * a.B * a.K_T * P;
-    const long long tid_raw = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool active = tid_raw < total;
-    const long long tid = active ? tid_raw : total - 1;   // inactive lanes mirror the last lane
-    const int p = (int)(tid % P);
-    long long r = tid / P;
-    const int k = (int)(r % a.K_T);
-    r /= a.K_T;
-    const int b = (int)(r % a.B);
-    const int l = (int)(r / a.B);
+    const int tpb = P < 64 ? 64 : P;            // lanes of a workgroup
+    const int k = blockIdx.x * (tpb / P) + (int)threadIdx.x / P;
+    const int p = (int)threadIdx.x % P;
+    const int b = blockIdx.y;
+    const int l = blockIdx.z;
+    const bool active = k < a.K_T;
+    const int kk = active ? k : a.K_T - 1;      // inactive lanes mirror a valid channel
     const int K = a.K;
 
     // Channel group of this lane inside the wave (P >= 16 >= M lanes per group).
@@ -40,22 +40,16 @@ decode_kernel(DecodeArgs a, int P) {
     const int G = P < 64 ? P : 64;
     const int base = lane - (lane % G);
     const int jm = (lane % G) < M ? (lane % G) : 0;
-    const size_t tab = ((size_t)l * K + k) * M;   // (layer, k, j=0) of rho/theta/c
-    float my_r, my_i;
-    {
-        const float rr = a.rho[tab + jm];
-        float sn, cs;
-        sincosf(a.theta[tab + jm], &sn, &cs);
-        my_r = rr * cs;
-        my_i = rr * sn;
-    }
+    const size_t tab = ((size_t)l * K + kk) * M;                 // (layer, k, j=0) of rho/theta/c
+    const size_t row = ((size_t)l * a.B + b) * K + kk;           // (layer, b, k)
 
-    const size_t row = ((size_t)l * a.B + b) * K + k;            // (layer, b, k)
+    // ---- every load first; the pole parameters first of all, so that waiting
+    // for them (loads complete in issue order) does not wait for the state --------------
+    const float rr = a.rho[tab + jm];
+    const float th = a.theta[tab + jm];
     const IO* vp = static_cast<const IO*>(a.v);
     const IO* gwp = static_cast<const IO*>(a.g_w);
     const IO* grp = static_cast<const IO*>(a.g_r);
-    const float x = io::load(vp, row * P + p);
-
     float* st = a.state + row * (size_t)(M * 2 * P) + p;
     float hr[M], hi[M];
 #pragma unroll
@@ -63,40 +57,50 @@ decode_kernel(DecodeArgs a, int P) {
         hr[j] = st[(2 * j) * P];
         hi[j] = st[(2 * j + 1) * P];
     }
+    const float x = io::load(vp, row * P + p);
+    float dl[PER_MODE ? M : 1], gw[PER_MODE ? M : 1], gr[PER_MODE ? M : 1];
+#pragma unroll
+    for (int j = 0; j < (PER_MODE ? M : 1); ++j) {
+        const size_t cj = PER_MODE ? row * M + j : row;
+        dl[j] = a.delta[cj];
+        gw[j] = io::load(gwp, cj);
+        gr[j] = io::load(grp, cj);
+    }
+    float cr[M], ci[M], za[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        cr[j] = a.c[(tab + j) * 2 + 0];
+        ci[j] = a.c[(tab + j) * 2 + 1];
+        za[j] = a.zl ? a.zl[tab + j] : 0.f;   // zero-lag correction (Eq. 24)
+    }
+
+    // ---- pole rotations, broadcast over the channel group ------------------------------------
+    float my_r, my_i;
+    {
+        float sn, cs;
+        sincosf(th, &sn, &cs);
+        my_r = rr * cs;
+        my_i = rr * sn;
+    }
 
     float acc = 0.f;
-    float e_ch = 0.f, w_ch = 0.f, g_ch = 0.f;
-    if (!PER_MODE) {
-        e_ch = expf(-a.delta[row]);
-        w_ch = io::load(gwp, row) * x;
-        g_ch = io::load(grp, row);
-    }
+    const float e_ch = PER_MODE ? 0.f : expf(-dl[0]);
+    const float w_ch = PER_MODE ? 0.f : gw[0] * x;
 #pragma unroll
     for (int j = 0; j < M; ++j) {
         const float pr = __shfl(my_r, base + j);
         const float pi = __shfl(my_i, base + j);
-        const float cr = a.c[(tab + j) * 2 + 0];
-        const float ci = a.c[(tab + j) * 2 + 1];
-        const float za = a.zl ? a.zl[tab + j] * cr : 0.f;   // zero-lag correction (Eq. 24)
-        float e, w, g;
-        if (PER_MODE) {
-            const size_t cj = row * M + j;
-            e = expf(-a.delta[cj]);
-            w = io::load(gwp, cj) * x;
-            g = io::load(grp, cj);
-        } else {
-            e = e_ch;
-            w = w_ch;
-            g = 1.f;
-        }
+        const float e = PER_MODE ? expf(-dl[PER_MODE ? j : 0]) : e_ch;
+        const float w = PER_MODE ? gw[PER_MODE ? j : 0] * x : w_ch;
+        const float g = PER_MODE ? gr[PER_MODE ? j : 0] : 1.f;
         const float ar = e * pr, ai = e * pi;
         const float nr = ar * hr[j] - ai * hi[j] + w;
         const float ni = ai * hr[j] + ar * hi[j];
         hr[j] = nr;
         hi[j] = ni;
-        acc += g * (cr * nr - ci * ni - za * w);
+        acc += g * (cr[j] * nr - ci[j] * ni - za[j] * cr[j] * w);
     }
-    if (!PER_MODE) acc *= g_ch;
+    if (!PER_MODE) acc *= gr[0];
 
     if (active) {
 #pragma unroll
@@ -110,14 +114,14 @@ decode_kernel(DecodeArgs a, int P) {
 
 template <int M, typename IO>
 hipError_t launch_decode_m(const DecodeArgs& a, int P, hipStream_t s) {
-    const long long total = (long long)a.n_layers * a.B * a.K_T * P;
-    if (total == 0) return hipSuccess;
-    const int threads = 256;
-    const unsigned blocks = (unsigned)((total + threads - 1) / threads);
+    if ((long long)a.n_layers * a.B * a.K_T == 0) return hipSuccess;
+    const int tpb = P < 64 ? 64 : P;
+    const int cpb = tpb / P;                     // channels per workgroup
+    const dim3 grid((unsigned)((a.K_T + cpb - 1) / cpb), (unsigned)a.B, (unsigned)a.n_layers);
     if (a.per_mode)
-        hipLaunchKernelGGL((decode_kernel<M, IO, true>), dim3(blocks), dim3(threads), 0, s, a, P);
+        hipLaunchKernelGGL((decode_kernel<M, IO, true>), grid, dim3(tpb), 0, s, a, P);
     else
-        hipLaunchKernelGGL((decode_kernel<M, IO, false>), dim3(blocks), dim3(threads), 0, s, a, P);
+        hipLaunchKernelGGL((decode_kernel<M, IO, false>), grid, dim3(tpb), 0, s, a, P);
     return hipGetLastError();
 }
 

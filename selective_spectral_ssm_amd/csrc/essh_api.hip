@@ -134,6 +134,7 @@ essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
         !aligned(g_r, io) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4) || (zl && !aligned(zl, 4)))
         return ESSH_ERR_INVALID_ARG;
     if ((long long)n_layers * d->B * d->K * d->P > (1LL << 30)) return ESSH_ERR_UNSUPPORTED;
+    if (d->B > 65535 || n_layers > 65535) return ESSH_ERR_UNSUPPORTED;   // grid y and z extents
     if (d->B == 0) return ESSH_OK;
 
     DecodeArgs a{};

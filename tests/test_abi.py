@@ -97,6 +97,9 @@ def test_decode_and_state_init_reject_bad_args(lib):
     assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 9), None, None) == essh.ESSH_ERR_INVALID_ARG
     assert lib.essh_mixer_decode_step(24, ctypes.byref(d), *([f] * 7), ctypes.c_void_p(FAKE + 2), f, f,
                                       None) == essh.ESSH_ERR_INVALID_ARG   # misaligned zl
+    assert lib.essh_mixer_decode_step(65536, ctypes.byref(d), *([f] * 10), None) == essh.ESSH_ERR_UNSUPPORTED
+    wide = essh.make_dims(65536, 1, 1, 1, 16, 1, 0)   # batch rows past the launch's grid extent
+    assert lib.essh_mixer_decode_step(1, ctypes.byref(wide), *([f] * 10), None) == essh.ESSH_ERR_UNSUPPORTED
     assert lib.essh_state_init(None, 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
     assert lib.essh_state_init(ctypes.c_void_p(FAKE + 4), 1, ctypes.byref(d), None) == essh.ESSH_ERR_INVALID_ARG
     assert lib.essh_mixer_prefill(None, *([f] * 12), 0, None) == essh.ESSH_ERR_INVALID_ARG
