@@ -167,12 +167,22 @@ struct __align__(16) Stage {
 };
 
 // Per-mode controls of a staged chunk (per-mode launches only): clock sums
-// * log2(e) and gates, [mode][position].
+// * log2(e) and gates, [mode][position], and the factors of the clock
+// referenced to the start T0 of each position's 16-position sub-block:
+//   fa[j][t] = g_r,j(t) e^{-(q_j(t) - q_j(T0-1))},  fb[j][s] = g_w,j(s) e^{q_j(s) - q_j(T0-1)}
+// (0 past the chunk's valid positions), so that g_r,j(t) e^{-(q_j(t)-q_j(s))} g_w,j(s)
+// = fa[j][t] fb[j][s] for t, s in one sub-block; ftr[j][T] = e^{-(q_j(T1) - q_j(T0-1))},
+// T1 the sub-block's last valid position; fexact[T] = 1 where some mode's clock
+// span over the sub-block is too large to factor.
 template <class C>
 struct __align__(16) StagePM {
     float q[C::M][C::LC];
     float gw[C::M][C::LC];
     float gr[C::M][C::LC];
+    float fa[C::M][C::LC];
+    float fb[C::M][C::LC];
+    float ftr[C::M][C::NSB];
+    int fexact[C::NSB];
 };
 
 // v tile of a staged chunk: [P/16][LC][16] bf16; y is staged in place.
@@ -841,6 +851,26 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 }
             }
             __syncthreads();
+            // factors of the clock referenced to each sub-block's start, per mode
+            for (int e = tid; e < M * LC; e += C::THREADS) {
+                const int j = e / LC, t = e - j * LC;
+                const int T0 = t & ~15;
+                const float d = spm.q[j][t] - (T0 > 0 ? spm.q[j][T0 - 1] : 0.f);   // >= 0 (log2 units)
+                spm.fa[j][t] = exp2f(-d) * spm.gr[j][t];
+                spm.fb[j][t] = t < n ? exp2f(d) * spm.gw[j][t] : 0.f;
+                if (t == min(T0 + 15, n - 1)) spm.ftr[j][t >> 4] = exp2f(-d);
+            }
+            for (int i = tid; i < C::NSB; i += C::THREADS) {
+                const int T0 = 16 * i, T1 = min(T0 + 15, n - 1);
+                int ex = 0;
+                if (T0 < n) {
+#pragma unroll
+                    for (int j = 0; j < M; ++j)
+                        if (spm.q[j][T1] - (T0 > 0 ? spm.q[j][T0 - 1] : 0.f) > SPAN2_FAST_MAX) ex = 1;
+                }
+                spm.fexact[i] = ex;
+            }
+            __syncthreads();
         }
     };
 
@@ -933,92 +963,173 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) lam[i] = at * l16[i];
         } else if constexpr (PM) {
-            // per-mode controls: every operand evaluated per element and mode,
-            // the read gate inside the sum over modes
+            // per-mode controls: operands per element and mode, the read gate
+            // inside the sum over modes
             //   G[t][s]  = sum_j g_r,j(t) e^{-(qj(t)-qj(s))} g_w,j(s) Re(c_j lambda_j^{t-s})  (s <= t)
             //   C[t][jr] = g_r,j(t) e^{-(qj(t)-qj(T0-1))} {Re, -Im}(c_j lambda_j^{t-T0+1})
             //   W[jr][s] = {Re, Im}(lambda_j^{T1-s}) e^{-(qj(T1)-qj(s))} g_w,j(s)
+            // from the staged factors fa, fb, ftr (products, no exponentials), or,
+            // where a mode's clock span is too large to factor, from the clock sums.
             const int T1 = min(T0 + 15, n - 1);
-            if (out) {
-                const int t = T0 + col;
-                float gv[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
+            if (spm.fexact[T] == 0) {
+                if (out) {
+                    const int t = T0 + col;
+                    float gv[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    const float qt = spm.q[j][t];
-                    const float grt = spm.gr[j][t];
+                    for (int j = 0; j < M; ++j) {
+                        const float fat = spm.fa[j][t];
+                        const float4 fb4 = *reinterpret_cast<const float4*>(&spm.fb[j][T0 + 4 * g]);
+                        const float fbs[4] = {fb4.x, fb4.y, fb4.z, fb4.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int sl = 4 * g + e;
-                        if (sl <= col) {
-                            const int s2 = T0 + sl;
-                            gv[e] += exp2f(spm.q[j][s2] - qt) * spm.gw[j][s2] * grt * sm.cpw[col - sl][j].x;
+                        for (int e = 0; e < 4; ++e) {
+                            const int sl = 4 * g + e;
+                            if (sl <= col) gv[e] += fat * fbs[e] * sm.cpw[col - sl][j].x;
                         }
                     }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * g + i, j = row >> 1;
+                        if (j < M) {
+                            const int jj = j < M ? j : 0;
+                            const float2 cp = sm.cpw[col + 1][jj];
+                            av[i] = spm.fa[jj][t] * ((row & 1) ? -cp.y : cp.x);
+                        }
+                    }
+                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
+                                                  make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        stage_y(T, nt, acc, 1.f);
+                    }
+                }
+                float wv[4];
+                {
+                    const int jr = col >> 1;
+                    const int jj = jr < M ? jr : 0;
+                    const float trj = spm.ftr[jj][T];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s2 = T0 + 4 * g + e;
+                        float val = 0.f;
+                        if (jr < M && s2 <= T1) {
+                            const float2 pw = sm.pw[T1 - s2][jj];
+                            val = ((col & 1) ? pw.y : pw.x) * spm.fb[jj][s2] * trj;
+                        }
+                        wv[e] = val;
+                    }
+                }
+                const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
+                const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
+                                              make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
+                                                         pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int j = 2 * g + hh;
+                    float2 pn = make_float2(0.f, 0.f);
+                    float at = 0.f;
+                    if (j < M) {
+                        const int jj = j < M ? j : 0;
+                        at = spm.ftr[jj][T];
+                        pn = sm.pw[T1 - T0 + 1][jj];
+                    }
+                    lam[2 * hh] = at * pn.x;
+                    lam[2 * hh + 1] = at * pn.y;
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * g + i, j = row >> 1;
+                for (int nt = 0; nt < NTW; ++nt) {
+                    f32x4_t d;
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const float hr = st[nt][i], hi = st[nt][i + 1];
+                        d[i] = lam[i] * hr - lam[i + 1] * hi;
+                        d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
+                    }
+                    st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
+                }
+            } else {
+                if (out) {
+                    const int t = T0 + col;
+                    float gv[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < M; ++j) {
+                        const float qt = spm.q[j][t];
+                        const float grt = spm.gr[j][t];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int sl = 4 * g + e;
+                            if (sl <= col) {
+                                const int s2 = T0 + sl;
+                                gv[e] += exp2f(spm.q[j][s2] - qt) * spm.gw[j][s2] * grt * sm.cpw[col - sl][j].x;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * g + i, j = row >> 1;
+                        if (j < M) {
+                            const int jj = j < M ? j : 0;
+                            const float qp = T0 > 0 ? spm.q[jj][T0 - 1] : 0.f;
+                            const float ea = exp2f(qp - spm.q[jj][t]) * spm.gr[jj][t];
+                            const float2 cp = sm.cpw[col + 1][jj];
+                            av[i] = ea * ((row & 1) ? -cp.y : cp.x);
+                        }
+                    }
+                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
+                                                  make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        stage_y(T, nt, acc, 1.f);
+                    }
+                }
+                float wv[4];
+                {
+                    const int jr = col >> 1;
+                    const int jj = jr < M ? jr : 0;
+                    const float qe = spm.q[jj][T1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s2 = T0 + 4 * g + e;
+                        float val = 0.f;
+                        if (jr < M && s2 <= T1) {
+                            const float2 pw = sm.pw[T1 - s2][jj];
+                            val = ((col & 1) ? pw.y : pw.x) * exp2f(spm.q[jj][s2] - qe) * spm.gw[jj][s2];
+                        }
+                        wv[e] = val;
+                    }
+                }
+                const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
+                const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
+                                              make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
+                                                         pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int j = 2 * g + hh;
+                    float2 pn = make_float2(0.f, 0.f);
+                    float at = 0.f;
                     if (j < M) {
                         const int jj = j < M ? j : 0;
                         const float qp = T0 > 0 ? spm.q[jj][T0 - 1] : 0.f;
-                        const float ea = exp2f(qp - spm.q[jj][t]) * spm.gr[jj][t];
-                        const float2 cp = sm.cpw[col + 1][jj];
-                        av[i] = ea * ((row & 1) ? -cp.y : cp.x);
+                        at = exp2f(qp - spm.q[jj][T1]);
+                        pn = sm.pw[T1 - T0 + 1][jj];
                     }
+                    lam[2 * hh] = at * pn.x;
+                    lam[2 * hh + 1] = at * pn.y;
                 }
-                const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
-                                              make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    stage_y(T, nt, acc, 1.f);
-                }
-            }
-            float wv[4];
-            {
-                const int jr = col >> 1;
-                const int jj = jr < M ? jr : 0;
-                const float qe = spm.q[jj][T1];
+                    f32x4_t d;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s2 = T0 + 4 * g + e;
-                    float val = 0.f;
-                    if (jr < M && s2 <= T1) {
-                        const float2 pw = sm.pw[T1 - s2][jj];
-                        val = ((col & 1) ? pw.y : pw.x) * exp2f(spm.q[jj][s2] - qe) * spm.gw[jj][s2];
+                    for (int i = 0; i < 4; i += 2) {
+                        const float hr = st[nt][i], hi = st[nt][i + 1];
+                        d[i] = lam[i] * hr - lam[i + 1] * hi;
+                        d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
                     }
-                    wv[e] = val;
+                    st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
                 }
-            }
-            const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
-            const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
-                                          make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
-                                                     pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int j = 2 * g + hh;
-                float2 pn = make_float2(0.f, 0.f);
-                float at = 0.f;
-                if (j < M) {
-                    const int jj = j < M ? j : 0;
-                    const float qp = T0 > 0 ? spm.q[jj][T0 - 1] : 0.f;
-                    at = exp2f(qp - spm.q[jj][T1]);
-                    pn = sm.pw[T1 - T0 + 1][jj];
-                }
-                lam[2 * hh] = at * pn.x;
-                lam[2 * hh + 1] = at * pn.y;
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                f32x4_t d;
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const float hr = st[nt][i], hi = st[nt][i + 1];
-                    d[i] = lam[i] * hr - lam[i + 1] * hi;
-                    d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
-                }
-                st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
             }
         } else {
             // exact path (ragged sub-block, or a clock span too large to factor):

@@ -161,6 +161,21 @@ def test_prefill_per_mode_chunked(name, widx, over, K_T, Lc):
     check_prefill(name + "_zero_lag", inp, K_T, Lc, zl=zl)
 
 
+@pytest.mark.parametrize("per_mode", [False, True], ids=["per_channel", "per_mode"])
+def test_prefill_large_clock_spans(per_mode):
+    """Clock spans too large to factor (Eq. 6's decay e^{-sum delta} far below fp32 range over a
+    sub-block) take the per-element path; the rest of the chunk keeps the factored one."""
+    w = I.workload(1, B=2, L=230, K=4)
+    inp = I.make_prefill_inputs(w, per_mode=per_mode)
+    d = inp["delta"]
+    d[:, 40:56] = 25.0            # every mode of every channel: a whole sub-block far past the limit
+    d[:, 97:101] = 12.0           # part of a sub-block
+    if per_mode:
+        d[:, 150:170, :, 1] = 30.0   # one mode only: the sub-blocks must still take the exact path
+    for Lc in (64, 128):
+        check_prefill(f"large_span_{'pm' if per_mode else 'pc'}_lc{Lc}", inp, w.K, Lc)
+
+
 def test_prefill_chunk_length_invariance():
     """Every chunk length gives the oracle's result (chunking is exact, Eq. 6)."""
     w = I.workload(1, B=1, L=257, K=3)
