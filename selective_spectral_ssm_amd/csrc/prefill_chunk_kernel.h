@@ -471,12 +471,13 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     if (SEG) {
         constexpr int CIA = (LC + 63) / 64;    // instructions per control array of a chunk
         constexpr int NCI = C::RES * 3 * CIA;
+        const int seg_last = min(c_end * LC, L) - 1;   // the segment's last position
 #pragma unroll
         for (int ci = 0; ci < NCI; ++ci) {
             const int i = ci / (3 * CIA), arr = (ci / CIA) % 3, u = ci % CIA;
             const int pos = u * 64 + lane;
             if (ci % C::NW == wave && pos < LC) {
-                const int t = min((c_begin + i) * LC + pos, L - 1);
+                const int t = i < nck ? min((c_begin + i) * LC + pos, L - 1) : seg_last;
                 const size_t row = ((size_t)b * L + t) * K + k;
                 Stage<C>* sp = stage_c(i);
                 if (arr == 0)
@@ -489,9 +490,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
 #pragma unroll
         for (int i = 0; i < C::RES; ++i) {
+            // rows past L repeat row L-1; a stage past the segment's chunks (never
+            // read) gets one row, so that every wave still issues TLW copies per stage
 #pragma unroll
-            for (int it = 0; it < TLW; ++it)   // rows past L: any valid row
-                copy_tile(stage_v(i), it, (c_begin + i) * LC, L);
+            for (int it = 0; it < TLW; ++it)
+                copy_tile(stage_v(i), it, i < nck ? (c_begin + i) * LC : seg_last, i < nck ? L : seg_last + 1);
         }
     }
 
