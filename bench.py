@@ -133,27 +133,35 @@ def copy_time_us(total_bytes, reps=50):
 
 
 def time_launches(fn, steps, warmup):
-    """Returns (ms per step over the whole timed region, mean ms per launch from per-launch events)."""
+    """Returns (ms per step over the whole timed region, mean and median ms per launch).
+
+    The timed region is `steps` back-to-back launches with nothing between them;
+    the per-launch durations come from a second pass of `steps` launches, each
+    bracketed by HIP events on the launch stream (events between launches add
+    a little time of their own, so they stay out of the timed region)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     # Keep the GPU busy while the host enqueues the timed launches, so that the
     # events measure back-to-back GPU execution and not host submission speed.
     torch.cuda._sleep(SLEEP_CYCLES)
     t0.record(s)
+    for _ in range(steps):
+        fn()
+    t1.record(s)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda._sleep(SLEEP_CYCLES)
     for a, b in ev:
         a.record(s)
         fn()
         b.record(s)
-    t1.record(s)
     torch.cuda.synchronize()
-    total = t0.elapsed_time(t1) / steps
     per = [a.elapsed_time(b) for a, b in ev]
     return total, statistics.mean(per), statistics.median(per)
 
