@@ -668,7 +668,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     Stage<C>* sgp = stage_c(0);   // staged chunk the helpers work on: factors
     uint16_t* sgv = stage_v(0);   // ... and v tile
     // element offset of (row r, first column of 16-byte unit u) in the v tile
-    auto vt_off = [&](int r, int u) __attribute__((always_inline)) { return (u >> 1) * C::TBLK + r * 16 + ((u & 1) << 3); };
+    auto vt_off = [&](int r, int u) __attribute__((always_inline)) {
+        return (u >> 1) * C::TBLK + r * 16 + ((u & 1) << 3);
+    };
 
     // Loads of one chunk held in registers until they are staged into LDS.
     // per-mode controls of a chunk spread over every thread: LC * M values each
@@ -913,12 +915,16 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
         bw_off[nt] = (wave * NTW + nt) * C::TBLK + lane * 4;
-    auto store_bv = [&](int T, int nt, uint2 x) __attribute__((always_inline)) { *reinterpret_cast<uint2*>(&sgv[bw_off[nt] + T * 256]) = x; };
+    auto store_bv = [&](int T, int nt, uint2 x) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(&sgv[bw_off[nt] + T * 256]) = x;
+    };
     auto load_bv = [&](int T, int nt) __attribute__((always_inline)) -> uint2 {
         return *reinterpret_cast<const uint2*>(&sgv[bw_off[nt] + T * 256]);
     };
 
-    auto hi4 = [&](const f32x4_t& x) __attribute__((always_inline)) -> uint2 { return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])); };
+    auto hi4 = [&](const f32x4_t& x) __attribute__((always_inline)) -> uint2 {
+        return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]));
+    };
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
@@ -1148,7 +1154,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sl = 4 * g + e;
-                    gv[e] = sl <= col ? exp2f(sgp->q2[T0 + sl] - qt) * bf16_to_f32((uint16_t)sgp->gw[T0 + sl]) * sm.psi[col - sl] : 0.f;
+                    gv[e] = sl <= col ? exp2f(sgp->q2[T0 + sl] - qt) * bf16_to_f32((uint16_t)sgp->gw[T0 + sl]) *
+                                            sm.psi[col - sl]
+                                      : 0.f;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1224,7 +1232,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // its end, Lambda_e = e^{-clock span}).  The state is carried once per block;
     // per sub-block only b(s) v(s) is formed (rounded to bf16) and fed to the
     // constant-operand products.
-    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb, float (&tr)[4]) __attribute__((always_inline)) {
+    auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb,
+                          float (&tr)[4]) __attribute__((always_inline)) {
         const float4 bk = sgp->blkB[Bi];
         uint2 hh[NTW];
         if (out) {
@@ -1347,7 +1356,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             if (tr < n) {
                 const size_t off = (((size_t)b * L + t) * K + k) * P + vcol0;
                 if constexpr (P >= 128 && MODE == MODE_STREAM)
-                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, outv), reinterpret_cast<u32x4_t*>(yg + off));
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, outv),
+                                                reinterpret_cast<u32x4_t*>(yg + off));
                 else
                     *reinterpret_cast<uint4*>(yg + off) = outv;
             }
@@ -1377,7 +1387,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     };
 
     // Look-back message rows: rows (j, re/im) of this lane's value columns.
-    auto publish = [&](float* dst, const f32x4_t (&s)[NTW], unsigned kind, const float (&trn)[4]) __attribute__((always_inline)) {
+    auto publish = [&](float* dst, const f32x4_t (&s)[NTW], unsigned kind,
+                       const float (&trn)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int p = wave * WCOLS + nt * 16 + col;
