@@ -60,6 +60,26 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_chunk_mixer370m_kt24.md")
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
+
+
+def measured_mfma_flops():
+    """MFMA flops per launch of the main prefill kernel (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
+    recorded for the current kernel source, else None."""
+    try:
+        text = open(MFMA_FILE).read()
+    except OSError:
+        return None
+    kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["mfma_flops_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def measured_traffic():
     """HBM bytes per launch recorded for the current kernel source, else None.
 
@@ -319,6 +339,7 @@ def main():
     log("prefill: mixer370m_prefill K_T=24")
     main_res, w, inp = prefill_case(1, 24, args.steps, args.warmup)
     traffic = measured_traffic()
+    mfma = measured_mfma_flops()
     copy_gbs = copy_bandwidth()
     log(f"plain copy: {copy_gbs:.0f} GB/s (read + write)")
     res = {
@@ -341,6 +362,10 @@ def main():
                      "frac": main_res["achieved_GBs"] / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic / (main_res["us_per_launch"] * 1e-6) / 1e9,
                      "traffic_bytes_per_launch": traffic,
+                     "mfma": None if mfma is None else {
+                         "flops_per_launch": mfma, "achieved": mfma / (main_res["us_per_launch"] * 1e-6) / 1e12,
+                         "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": mfma / (main_res["us_per_launch"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS},
                      "alg_bytes_per_launch": main_res["alg_bytes"],
                      "copy_GBs": copy_gbs, "frac_of_copy": main_res["achieved_GBs"] / copy_gbs,
                      "copy_same_bytes_us": copy_time_us(main_res["alg_bytes"]),
