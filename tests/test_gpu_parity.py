@@ -48,8 +48,8 @@ def check_prefill(name, inp, K_T, Lc=0, state_in=None, zl=None):
     zo = None if zl is None else np.asarray(zl, np.float32).astype(np.float64)
     y_ref, s_ref = oracle.prefill(**ox, K_T=K_T, state_in=state_in, zl=zo)
     tol = TOL[inp["io"]]
-    ey = block_err(to_host_f64(y)[:, :, :K_T], y_ref[:, :, :K_T], chan_axis=2)
-    es = block_err(to_host_f64(st)[:, :K_T], s_ref[:, :K_T], chan_axis=1)
+    ey = block_err(to_host_f64(y[:, :, :K_T]), y_ref[:, :, :K_T], chan_axis=2)
+    es = block_err(to_host_f64(st[:, :K_T]), s_ref[:, :K_T], chan_axis=1)
     log(f"{name}: y err {ey:.3e}, state err {es:.3e} (tol {tol:g})")
     assert ey <= tol, f"{name} K_T={K_T}: y error {ey:.3e} > {tol}"
     assert es <= tol, f"{name} K_T={K_T}: state error {es:.3e} > {tol}"
@@ -366,8 +366,8 @@ def test_decode_step_matches_oracle(io, per_mode, m, P):
         y_ref, s_ref = oracle.decode_step(state.astype(np.float64), **ox, K_T=K_T,
                                           zl=zl.astype(np.float64) if zero_lag else None)
         tol = TOL[io]
-        ey = block_err(to_host_f64(y)[:, :, :K_T].reshape(-1, K_T, P), y_ref[:, :, :K_T].reshape(-1, K_T, P), 1)
-        es = block_err(to_host_f64(st)[:, :, :K_T].reshape(-1, K_T, m * 2 * P),
+        ey = block_err(to_host_f64(y[:, :, :K_T]).reshape(-1, K_T, P), y_ref[:, :, :K_T].reshape(-1, K_T, P), 1)
+        es = block_err(to_host_f64(st[:, :, :K_T]).reshape(-1, K_T, m * 2 * P),
                        s_ref[:, :, :K_T].reshape(-1, K_T, m * 2 * P), 1)
         log(f"  y err {ey:.3e}, state err {es:.3e}")
         assert ey <= tol and es <= tol
