@@ -131,15 +131,20 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
     p.nseq = B * K_T;
     p.nchunks = (L + Lc - 1) / Lc;
     if (p.nseq == 0 || p.nchunks == 0) return p;
-    // With about 1.5 sequences per CU or more, whole sequences keep the GPU
-    // busy.  Below that, sequences are cut into segments of as many chunks as
+    // With about 1.5 sequences per CU or more (one per CU when P = 128), whole
+    // sequences keep the GPU busy.  Below that, sequences are cut into segments of as many chunks as
     // a workgroup keeps resident in LDS, and a look-back scan links them.
     // With very few sequences a round of resident workgroups (about 1000)
     // covers many segments of each sequence, so each look-back would fold
     // dozens of predecessors; there the three-launch scan is used instead,
     // with about SPLIT_TARGET segments overall (at most what one scan
     // workgroup composes per sequence).
-    constexpr int SEQ_ENOUGH = 384;
+    // Whole sequences from SEQ_ENOUGH sequences up: 384, or 256 when P = 128,
+    // whose sequences carry twice the work per wave.  Measured on MI355X: P = 128
+    // streams 256 whole sequences in 82 us against the look-back's 104 us, and 128
+    // in 80 us against 51; P = 64 keeps the look-back at 192 sequences (41 us
+    // against 63).
+    const int SEQ_ENOUGH = P >= 128 ? 256 : 384;
     constexpr int SPLIT_MAX_SEQ = 32;
     constexpr int SPLIT_TARGET = 1536;
     int seg_chunks = p.nchunks;
