@@ -83,9 +83,12 @@ def test_prefill_reduced(name, widx, over, tiers, Lc):
 
 # Both ways of linking segments of a sequence: the three-launch scan (few
 # sequences; here 40 segments, so the segment scan composes three groups of 16)
-# and the single-launch look-back scan (40 sequences of 18 resident segments).
+# and the single-launch look-back scan (40 sequences of 18 resident segments,
+# whose tickets give each XCD's counter a contiguous range of sequences; and 39
+# sequences, not a multiple of the eight counters, whose tickets interleave).
 SEGMENT_SCANS = [("three_launch_40_segments", dict(B=1, L=64 * 40 - 7, K=2), 2),
-                 ("lookback_18_segments", dict(B=5, L=64 * 70 + 9, K=8), 8)]
+                 ("lookback_18_segments", dict(B=5, L=64 * 70 + 9, K=8), 8),
+                 ("lookback_39_sequences_interleaved", dict(B=3, L=64 * 20 + 5, K=16), 13)]
 
 
 @pytest.mark.parametrize("name,over,K_T", SEGMENT_SCANS, ids=[c[0] for c in SEGMENT_SCANS])
