@@ -12,7 +12,8 @@ full tier K_T=24, inputs resident in HBM.  ``value`` is tokens per second
   * cpu_baseline: the fp64 CPU oracle (OpenMP over sequences) on the same workload;
   * decode: the 24-layer batch-one decode workload (K=32, m=8, P=128, K_T=32),
     1024 steps replayed from a HIP graph, us/step and kernel roofline;
-  * extra: tier sweeps of the three prefill workloads.
+  * extra: tier sweeps of the three prefill workloads, the per-mode control form, and the
+    decode at tiers K_T = 8, 16, 24 beside 32.
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -220,8 +221,12 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
     import torch
     from selective_spectral_ssm_amd import essh, inputs as I, sizes
     w = I.workload(3)
-    log(f"decode: drawing inputs ({w.layers} layers, context {context}, {n_steps} steps)")
-    dec = I.make_decode_inputs(w, n_steps=n_steps, context=context)
+    key = ("decode", n_steps, context)
+    if key not in _CACHE:
+        log(f"decode: drawing inputs ({w.layers} layers, context {context}, {n_steps} steps)")
+        _CACHE.clear()
+        _CACHE[key] = I.make_decode_inputs(w, n_steps=n_steps, context=context)
+    dec = _CACHE[key]
     NL = w.layers
     rho, theta, c = to_dev(dec["rho"]), to_dev(dec["theta"]), to_dev(dec["c"])
     state = torch.zeros((NL, 1, w.K, w.m, 2, w.P), device="cuda")
@@ -391,6 +396,18 @@ def main():
             pm.append({k: r[k] for k in ("workload", "K_T", "us_per_launch", "kernel_tokens_per_s", "achieved_GBs")})
             pm[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
         res["prefill_per_mode"] = pm
+        if not args.no_decode:
+            dt = []
+            for kt in (8, 16, 24):
+                log(f"decode tier sweep: K_T={kt}")
+                r = decode_case(kt)
+                dt.append({"K_T": kt, "us_per_step_graph": r["us_per_step_graph"],
+                           "alg_bytes_per_step": r["alg_bytes_per_step"], "achieved_GBs": r["achieved_GBs"],
+                           "frac": r["frac_of_hbm_peak"]})
+            dt.append({"K_T": 32, "us_per_step_graph": res["decode"]["us_per_step_graph"],
+                       "alg_bytes_per_step": res["decode"]["alg_bytes_per_step"],
+                       "achieved_GBs": res["decode"]["achieved_GBs"], "frac": res["decode"]["frac_of_hbm_peak"]})
+            res["decode_tiers"] = dt
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, w, 24)
