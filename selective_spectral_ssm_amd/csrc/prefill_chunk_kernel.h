@@ -1367,8 +1367,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // staged y -> global by whole rows, non-temporally: each 128-byte line is
     // written by one instruction, so none is left dirty in L2 when the kernel
     // ends.  Needs every wave's y of the chunk staged (a barrier before).  Used
-    // by the look-back launch with P <= 64 (measured faster there; with wider
-    // rows the read-back crosses too many tile blocks).
+    // with P <= 64 by the look-back launch and the streaming launch (measured
+    // faster there; with wider rows the read-back crosses too many tile blocks).
     auto store_y_rows = [&](int t0, int n) __attribute__((always_inline)) {
         constexpr int UPR = P / 8;                     // 16-byte units per row
         constexpr int RPW = 64 / UPR;                  // rows per wave instruction
@@ -1670,13 +1670,27 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const int t0 = c * LC;
             const int n = min(LC, L - t0);
             __builtin_amdgcn_s_waitcnt(WAIT_VMEM0);   // loads of chunk c, issued a chunk ago
-            if (!AGG && yt0 >= 0) store_y(yt0, yn);  // each wave reads back only its own columns
+            if (!AGG && yt0 >= 0) {
+                if constexpr (P <= 64 && MODE == MODE_STREAM) {
+                    lds_barrier();   // every wave's y of chunk c-1 is staged
+                    store_y_rows(yt0, yn);
+                } else {
+                    store_y(yt0, yn);   // each wave reads back only its own columns
+                }
+            }
             stage_chunk(rb, n, c + 1 < c_end ? c + 1 : -1);
             chunk_pass(st, n, !AGG, tr);
             yt0 = t0;
             yn = n;
         }
-        if (!AGG && yt0 >= 0) store_y(yt0, yn);
+        if (!AGG && yt0 >= 0) {
+            if constexpr (P <= 64 && MODE == MODE_STREAM) {
+                lds_barrier();
+                store_y_rows(yt0, yn);
+            } else {
+                store_y(yt0, yn);
+            }
+        }
     }
 
     // ---- segment aggregate (three-launch scan) ----------------------------------------------
