@@ -100,6 +100,31 @@ def test_prefill_segment_scans(name, over, K_T):
     check_prefill(name, inp, K_T, 64, state_in=s0)
 
 
+# The look-back scan and whole-sequence streaming at the other (P, m, Lc)
+# instantiations.  B*K_T sequences pick the form: 40 or 48 (between 32 and the
+# whole-sequence threshold) take the look-back, with segments of as many chunks
+# as fit the 40 KB residency budget (4 for P=16/Lc=32 and P=128/Lc=32, 3 for
+# P=32/Lc=128, 2 for P=64/Lc=128, 1 for P=128/Lc=128); 384 sequences (256 with
+# P=128) stream whole.  Every case has a ragged last chunk and an entering state.
+SHAPE_SCANS = [("lookback_m1_p16_lc32", 1, dict(B=4, L=32 * 13 + 3, K=12, m=1, P=16), 12, 32),
+               ("lookback_m2_p32_lc128", 1, dict(B=4, L=128 * 7 + 9, K=12, m=2, P=32), 12, 128),
+               ("lookback_m8_p64_lc128", 1, dict(B=5, L=128 * 5 + 7, K=8, m=8, P=64), 8, 128),
+               ("lookback_m8_p128_lc128", 2, dict(B=5, L=128 * 3 + 7, K=8), 8, 128),
+               ("lookback_m4_p128_lc32", 2, dict(B=5, L=32 * 9 + 1, K=8, m=4), 8, 32),
+               ("whole_m1_p16_lc32", 1, dict(B=16, L=32 * 3 + 5, K=24, m=1, P=16), 24, 32),
+               ("whole_m2_p32_lc128", 1, dict(B=16, L=128 * 2 + 3, K=24, m=2, P=32), 24, 128),
+               ("whole_m8_p128_lc128", 2, dict(B=8, L=128 * 2 + 3, K=32), 32, 128)]
+
+
+@pytest.mark.parametrize("name,widx,over,K_T,Lc", SHAPE_SCANS, ids=[c[0] for c in SHAPE_SCANS])
+def test_prefill_scan_forms_all_shapes(name, widx, over, K_T, Lc):
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w)
+    rng = np.random.default_rng(17)
+    s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    check_prefill(name, inp, K_T, Lc, state_in=s0)
+
+
 # Zero-lag correction (App. C.3, Eq. 24) on every prefill path: the look-back
 # and whole-sequence MFMA kernels (per-channel bf16), the three-launch scan,
 # the sequential kernel (fp32 io) and the per-mode MFMA scan.
