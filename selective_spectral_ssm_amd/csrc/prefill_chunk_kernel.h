@@ -292,10 +292,22 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
 // AGG_PM are STREAM and AGG with clock and gates per mode ([B, L, K, m], Eq. 5).
 enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2, MODE_STREAM_PM = 3, MODE_AGG_PM = 4 };
 
+// Workgroups per CU that the register budget is held to.  Look-back launches
+// keep a workgroup's chunks resident in LDS, four workgroups per CU, and match
+// that.  Per-mode launches with up to four modes fit three workgroups in 168
+// VGPRs without spilling.  On MI355X that made the per-mode three-launch scan
+// 16-17% faster than the unbounded two (370M-class, K_T = 6..24); four
+// spilled and was slower.
 template <class C, int MODE>
-// Segmented launches keep a workgroup's chunks resident in LDS (four
-// workgroups per CU); the register budget is held to match that occupancy.
-__global__ void __launch_bounds__(C::THREADS, MODE == MODE_LOOKBACK && C::NW == 4 && C::M <= 4 ? 4 : 1)
+constexpr int min_workgroups_per_cu() {
+    if (C::NW != 4 || C::M > 4) return 1;
+    if (MODE == MODE_LOOKBACK) return 4;
+    if (MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM) return 3;
+    return 1;
+}
+
+template <class C, int MODE>
+__global__ void __launch_bounds__(C::THREADS, (min_workgroups_per_cu<C, MODE>()))
 prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr int LC = C::LC, M = C::M, P = C::P, WCOLS = C::WCOLS, NTW = C::NTW;
     constexpr int ROWS = 2 * M;          // state rows (mode, re/im) per value column
