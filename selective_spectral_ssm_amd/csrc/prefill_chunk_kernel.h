@@ -294,15 +294,16 @@ enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2, MODE_STREAM_PM = 3, MOD
 
 // Workgroups per CU that the register budget is held to.  Look-back launches
 // keep a workgroup's chunks resident in LDS, four workgroups per CU, and match
-// that.  Per-mode launches with up to four modes fit three workgroups in 168
-// VGPRs without spilling.  On MI355X that made the per-mode three-launch scan
-// 16-17% faster than the unbounded two (370M-class, K_T = 6..24); four
-// spilled and was slower.
+// that.  Streaming and per-mode launches with up to four modes fit three
+// workgroups in 168 VGPRs without spilling.  Measured on MI355X against the
+// unbounded two: the per-mode three-launch scan 16-17% faster (370M-class,
+// K_T = 6..24), the 128K-token three-launch scan 2-10% faster (K_T = 24..6).
+// Four spilled and was slower.
 template <class C, int MODE>
 constexpr int min_workgroups_per_cu() {
     if (C::NW != 4 || C::M > 4) return 1;
     if (MODE == MODE_LOOKBACK) return 4;
-    if (MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM) return 3;
+    if (MODE == MODE_STREAM || MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM) return 3;
     return 1;
 }
 
