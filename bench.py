@@ -3,13 +3,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
-A step is one chunked prefill call over the 370M-class mixer-layer workload
-(B=8, L=2048, K=24, m=4, P=64, Lc=64, bf16 v/gates, fp32 clock and state),
-full tier K_T=24, inputs resident in HBM.  ``value`` is tokens per second
-(B*L per step).  The same JSON line also carries
-  * roofline: algorithmic bytes of one prefill launch / its average duration
-    (HIP events around each launch on the launch stream) against 8 TB/s;
-  * cpu_baseline: the fp64 CPU oracle (OpenMP over sequences) on the same workload;
+A step is one chunked prefill call over the largest single-GPU workload, the
+128K-token DNA-like prefill (B=1, L=131072, K=24, m=4, P=64, Lc=128, bf16 v/gates,
+fp32 clock and state), full tier K_T=24, inputs resident in HBM.  ``value`` is
+tokens per second (B*L per step).  The same JSON line also carries
+  * roofline: algorithmic bytes of one prefill call / its average duration (HIP
+    events around each call on the launch stream) against 8 TB/s;
+  * cpu_baseline: the CPU oracle (float32, -O3 -march=native, OpenMP over sequences)
+    on the same workload, all host cores and one;
   * decode: the 24-layer batch-one decode workload (K=32, m=8, P=128, K_T=32),
     1024 steps replayed from a HIP graph, us/step and kernel roofline;
   * extra: tier sweeps of the three prefill workloads, the per-mode control form, and the
@@ -23,6 +24,7 @@ import json
 import os
 import re
 import statistics
+import subprocess
 import sys
 import time
 
@@ -31,11 +33,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 SLEEP_CYCLES = 200_000_000
-# HBM bytes per launch of the main prefill kernel, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes scaled by the same counters on a plain copy of known size.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_chunk_mixer370m_kt24.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
-                  for f in ("prefill_chunk_kernel.h", "prefill_chunk.hip", "essh_internal.h")]
+# Summaries of rocprofv3 runs committed under profiles/: HBM bytes per launch from FETCH_SIZE
+# and WRITE_SIZE passes (scaled by the same counters on a plain copy of known size), MFMA flops
+# per launch, and the decode kernel's median duration.  Each records the SHA-256 of the kernel
+# sources it was taken on and is used only while they still hash to it.
+PREFILL_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
+                   for f in ("prefill_chunk_kernel.h", "prefill_chunk.hip", "essh_internal.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
+                  for f in ("decode.hip", "essh_internal.h")]
+# The headline: the largest single-GPU workload (128K-token DNA-like prefill) at its full tier.
+HEADLINE = (4, 24)
 METRIC = "selective spectral scan prefill tokens/s + decode µs/step, % of HBM roofline"
 
 
@@ -52,49 +59,30 @@ def to_dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def kernel_source_hash():
+def source_hash(files):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_chunk_mixer370m_kt24.md")
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 
 
-def measured_mfma_flops():
-    """MFMA flops per launch of the main prefill kernel (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
-    recorded for the current kernel source, else None."""
+def profile_value(name, key, sources):
+    """A number recorded in profiles/<name>.md (a line "- key: `value`"), or None when the file
+    is missing or was taken on kernel sources that no longer hash to its source_sha256."""
     try:
-        text = open(MFMA_FILE).read()
+        text = open(os.path.join(ROOT, "profiles", name + ".md")).read()
     except OSError:
         return None
     kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
-    if kv.get("source_sha256") != kernel_source_hash():
+    if kv.get("source_sha256") != source_hash(sources):
         return None
     try:
-        return float(kv["mfma_flops_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-def measured_traffic():
-    """HBM bytes per launch recorded for the current kernel source, else None.
-
-    The counters only describe the kernel they were taken on: when the source
-    hash recorded beside them differs from the current one, traffic is unknown."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
-    if kv.get("source_sha256") != kernel_source_hash():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -209,6 +197,7 @@ def prefill_case(widx, K_T, steps, warmup, per_mode=False):
     call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
                         K_T=K_T, Lc=w.Lc, want_state=True)
     ms_step, ms_launch, ms_med = time_launches(call.run, steps, warmup)
+    call.check()                 # a look-back wait that ran out would have made the outputs invalid
     nbytes = sizes.prefill_bytes(w.B, w.L, K_T, w.m, w.P, w.io, write_state=True, per_mode=per_mode)
     return dict(workload=w.name, K_T=K_T, ms_per_step=ms_step, us_per_launch=ms_launch * 1e3,
                 us_per_launch_median=ms_med * 1e3,
@@ -279,6 +268,8 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
         times.append((time.perf_counter() - t0) * 1e6 / n_steps)
     nbytes = sizes.decode_bytes(NL, 1, K_T, w.m, w.P, "bf16")
     kmean = statistics.mean(per)
+    # the decode kernel's own median duration, from the committed rocprofv3 kernel trace
+    k_rocprof = profile_value("kernel_trace_decode_mixer1p5b", f"median_us_kt{K_T}", DECODE_SOURCES)
     # Achieved bandwidth from the graph replay: one kernel per step back to back, so the
     # per-step time is the kernel plus the gap to the next one.  Events around each
     # eager launch add their own overhead to a kernel this short and read higher.
@@ -286,48 +277,87 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
     return dict(workload=w.name, layers=NL, K_T=K_T, steps=n_steps, copy_same_bytes_us=copy_time_us(nbytes),
                 us_per_step_graph=us_step, us_per_step_graph_all=times,
                 us_per_kernel_mean=kmean, us_per_kernel_median=statistics.median(per),
+                us_per_kernel_rocprof_median=k_rocprof,
+                frac_of_hbm_peak_kernel=None if k_rocprof is None else nbytes / (k_rocprof * 1e-6) / 1e9 / HBM_PEAK_GBS,
                 alg_bytes_per_step=nbytes, achieved_GBs=nbytes / (us_step * 1e-6) / 1e9,
                 frac_of_hbm_peak=nbytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
                 achieved_GBs_eager_events=nbytes / (kmean * 1e-6) / 1e9)
 
 
-def cpu_baseline(inp, w, K_T, budget_s=10.0, max_runs=2000):
-    """The fp64 CPU oracle, as the parity tests use it, on the whole main workload.
+def _lscpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
 
-    The workload takes a small fraction of a second on the host, so the sample
-    is that whole workload repeated for about budget_s seconds; the median run
-    gives the rate."""
+
+def cpu_baseline(inp, w, K_T, runs=5):
+    """The CPU oracle timed on this host, as the benchmark spec plans it: the oracle's C source built
+    as float32 with -O3 -march=native for this host, OpenMP over the independent (batch row,
+    channel) sequences on every host core, median of `runs` runs after one warm-up; the same
+    on one thread; and the decode step (24 layers) on all cores.  A reported baseline only."""
+    import numpy as np
+
     import oracle
     from selective_spectral_ssm_amd.inputs import as_f64
-    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-    nthreads = max(1, min(nthreads, 16))
-    x = dict(v=as_f64(inp["v"], w.io), delta=inp["delta"].astype("float64"),
-             g_w=as_f64(inp["g_w"], w.io), g_r=as_f64(inp["g_r"], w.io),
-             rho=inp["rho"].astype("float64"), theta=inp["theta"].astype("float64"),
-             c=inp["c"].astype("float64"))
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < max_runs and (time.perf_counter() - t_start) < budget_s:
-        t0 = time.perf_counter()
-        oracle.prefill(**x, K_T=K_T, nthreads=nthreads)
-        times.append(time.perf_counter() - t0)
-    med = statistics.median(times)
-    elapsed = time.perf_counter() - t_start
-    cores = oracle.threads_used("f64")
-    # the same oracle on one host thread, over a shorter sample
-    t1s = []
-    t_start1 = time.perf_counter()
-    while len(t1s) < max_runs and (time.perf_counter() - t_start1) < budget_s / 3:
-        t0 = time.perf_counter()
-        oracle.prefill(**x, K_T=K_T, nthreads=1)
-        t1s.append(time.perf_counter() - t0)
-    med1 = statistics.median(t1s)
-    return dict(value=w.B * w.L / med, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"whole {w.name} workload (B={w.B}, L={w.L}, K_T={K_T}), fp64 oracle, "
-                       f"median of {len(times)} runs over {elapsed:.1f} s",
-                seconds_per_run=med,
-                single_thread=dict(value=w.B * w.L / med1, cores=1, seconds_per_run=med1,
-                                   sample=f"median of {len(t1s)} runs on one thread"))
+    so = oracle.build_native(os.path.join(ROOT, "oracle", "_build"))
+    run = oracle.make_prefill(so_path=so, precision="f32")
+    ncores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    x = dict(v=as_f64(inp["v"], w.io).astype(np.float32), delta=inp["delta"],
+             g_w=as_f64(inp["g_w"], w.io).astype(np.float32), g_r=as_f64(inp["g_r"], w.io).astype(np.float32),
+             rho=inp["rho"], theta=inp["theta"], c=inp["c"])
+
+    def timed(nthreads, kt):
+        ts = []
+        for i in range(runs + 1):
+            t0 = time.perf_counter()
+            run(**x, K_T=kt, nthreads=nthreads)
+            if i > 0:                       # the first run is the warm-up
+                ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    med = timed(ncores, K_T)
+    cores = oracle.threads_used("f32", so_path=so)
+    # one thread: a bounded sample, the first kt1 of the K_T channels (every channel is the same
+    # amount of work), scaled to the whole tier
+    kt1 = max(1, min(K_T, (2 * w.B * 131072) // (w.B * w.L) if w.L else K_T))
+    med1 = timed(1, kt1) * K_T / kt1
+    nb = w.B * w.L
+    res = dict(value=nb / med, unit="tokens/s", cores=cores, kind="oracle",
+               sample=f"whole {w.name} workload (B={w.B}, L={w.L}, K_T={K_T}), float32 oracle built -O3 "
+                      f"-march=native, OpenMP over (b, k) sequences, median of {runs} runs after 1 warm-up",
+               cpu_model=_lscpu_model(), nproc=ncores, seconds_per_run=med,
+               single_thread=dict(value=nb / med1, cores=1, seconds_per_run=med1,
+                                  sample=f"one thread, the first {kt1} of the {K_T} channels of every batch row "
+                                         f"(median of {runs} runs after 1 warm-up), scaled by {K_T}/{kt1}"))
+    # decode: the 24-layer step (K_T = 32) on all cores, over a bounded number of steps
+    from selective_spectral_ssm_amd import inputs as I
+    wd = I.workload(3)
+    n_steps = 16
+    dec = I.make_decode_inputs(wd, n_steps=n_steps + 1, context=1)
+    st = np.zeros((wd.layers, 1, wd.K, wd.m, 2, wd.P), np.float32)
+
+    def dstep(s, st):
+        ys, sts = [], []
+        for l in range(wd.layers):
+            y, s2 = run(as_f64(dec["step_v"][s, l][:, None], "bf16").astype(np.float32),
+                        dec["step_delta"][s, l][:, None], as_f64(dec["step_g_w"][s, l][:, None], "bf16"),
+                        as_f64(dec["step_g_r"][s, l][:, None], "bf16"), dec["rho"][l], dec["theta"][l],
+                        dec["c"][l], state_in=st[l], nthreads=ncores)
+            sts.append(s2)
+        return np.stack(sts)
+    st = dstep(0, st)                        # warm-up
+    t0 = time.perf_counter()
+    for s in range(1, n_steps + 1):
+        st = dstep(s, st)
+    res["decode_us_per_step"] = (time.perf_counter() - t0) / n_steps * 1e6
+    res["decode_sample"] = (f"{n_steps} steps of the 24-layer decode (K=K_T=32, m=8, P=128, B=1), "
+                            f"float32 oracle on {ncores} threads, after 1 warm-up step")
+    return res
 
 
 def main():
@@ -353,12 +383,17 @@ def main():
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
 
-    log("prefill: mixer370m_prefill K_T=24")
-    main_res, w, inp = prefill_case(1, 24, args.steps, args.warmup)
-    traffic = measured_traffic()
-    mfma = measured_mfma_flops()
+    widx, KT = HEADLINE
+    from selective_spectral_ssm_amd import inputs as I
+    wname = I.WORKLOADS[widx].name
+    log(f"prefill: {wname} K_T={KT}")
+    main_res, w, inp = prefill_case(widx, KT, args.steps, args.warmup)
+    tag = f"prefill_{wname.replace('_prefill', '')}_kt{KT}"
+    traffic = profile_value("hbm_traffic_" + tag, "hbm_bytes_per_launch", PREFILL_SOURCES)
+    mfma = profile_value("mfma_" + tag, "mfma_flops_per_launch", PREFILL_SOURCES)
     copy_gbs = copy_bandwidth()
     log(f"plain copy: {copy_gbs:.0f} GB/s (read + write)")
+    us = main_res["us_per_launch"]
     res = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -372,39 +407,42 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "L": w.L, "K": w.K, "K_T": 24, "m": w.m, "P": w.P,
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "K": w.K, "K_T": KT, "m": w.m, "P": w.P,
                    "Lc": w.Lc, "io": w.io, "state": "fp32", "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel",
+        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel (every launch of one essh_mixer_prefill call)",
                      "achieved": main_res["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": main_res["achieved_GBs"] / HBM_PEAK_GBS,
-                     "traffic": None if traffic is None else traffic / (main_res["us_per_launch"] * 1e-6) / 1e9,
+                     "traffic": None if traffic is None else traffic / (us * 1e-6) / 1e9,
                      "traffic_bytes_per_launch": traffic,
                      "mfma": None if mfma is None else {
-                         "flops_per_launch": mfma, "achieved": mfma / (main_res["us_per_launch"] * 1e-6) / 1e12,
+                         "flops_per_launch": mfma, "achieved": mfma / (us * 1e-6) / 1e12,
                          "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": mfma / (main_res["us_per_launch"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS},
+                         "frac": mfma / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS},
                      "alg_bytes_per_launch": main_res["alg_bytes"],
                      "copy_GBs": copy_gbs, "frac_of_copy": main_res["achieved_GBs"] / copy_gbs,
                      "copy_same_bytes_us": copy_time_us(main_res["alg_bytes"]),
-                     "us_per_launch": main_res["us_per_launch"]},
+                     "us_per_launch": us},
     }
     if not args.no_decode:
         log("decode: 24 layers K_T=32")
         res["decode"] = decode_case(32)
     if not args.no_extra:
         extra = []
-        for widx, tiers in ((1, (6, 12, 18)), (2, (8, 16, 24, 32)), (4, (6, 12, 18, 24))):
-            for kt in tiers:
-                log(f"tier sweep: workload {widx} K_T={kt}")
-                r, _, _ = prefill_case(widx, kt, max(10, args.steps // 4), 5)
+        for wi in (1, 2, 4):
+            for kt in I.WORKLOADS[wi].tiers:
+                if (wi, kt) == HEADLINE:
+                    r = main_res
+                else:
+                    log(f"tier sweep: workload {wi} K_T={kt}")
+                    r, _, _ = prefill_case(wi, kt, max(10, args.steps // 4), 5)
                 extra.append({k: r[k] for k in ("workload", "K_T", "us_per_launch", "kernel_tokens_per_s",
                                                 "achieved_GBs")})
                 extra[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
         res["prefill_tiers"] = extra
         pm = []
-        for widx, kt in ((1, 24), (2, 32), (2, 8)):
-            log(f"per-mode controls: workload {widx} K_T={kt}")
-            r, _, _ = prefill_case(widx, kt, max(10, args.steps // 4), 5, per_mode=True)
+        for wi, kt in ((1, 24), (2, 32), (2, 8)):
+            log(f"per-mode controls: workload {wi} K_T={kt}")
+            r, _, _ = prefill_case(wi, kt, max(10, args.steps // 4), 5, per_mode=True)
             pm.append({k: r[k] for k in ("workload", "K_T", "us_per_launch", "kernel_tokens_per_s", "achieved_GBs")})
             pm[-1]["frac"] = r["achieved_GBs"] / HBM_PEAK_GBS
         res["prefill_per_mode"] = pm
@@ -413,16 +451,14 @@ def main():
             for kt in (8, 16, 24):
                 log(f"decode tier sweep: K_T={kt}")
                 r = decode_case(kt)
-                dt.append({"K_T": kt, "us_per_step_graph": r["us_per_step_graph"],
-                           "alg_bytes_per_step": r["alg_bytes_per_step"], "achieved_GBs": r["achieved_GBs"],
-                           "frac": r["frac_of_hbm_peak"]})
-            dt.append({"K_T": 32, "us_per_step_graph": res["decode"]["us_per_step_graph"],
-                       "alg_bytes_per_step": res["decode"]["alg_bytes_per_step"],
-                       "achieved_GBs": res["decode"]["achieved_GBs"], "frac": res["decode"]["frac_of_hbm_peak"]})
+                dt.append({k: r[k] for k in ("K_T", "us_per_step_graph", "alg_bytes_per_step", "achieved_GBs",
+                                             "frac_of_hbm_peak", "us_per_kernel_rocprof_median",
+                                             "frac_of_hbm_peak_kernel")})
+            dt.append({k: res["decode"][k] for k in dt[0]})
             res["decode_tiers"] = dt
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(inp, w, 24)
+        res["cpu_baseline"] = cpu_baseline(inp, w, KT)
     print(json.dumps(res))
 
 

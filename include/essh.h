@@ -131,9 +131,15 @@ size_t essh_prefill_workspace_bytes(const essh_dims* d);
  *                        that share one workspace must be ordered (one
  *                        stream, or events): concurrent calls on one
  *                        workspace race.  Every wait inside the scan is
- *                        bounded; if one ever runs out, the kernel sets
- *                        32-bit word 1 of the workspace to a nonzero error
- *                        code and that call's y and state_out are invalid.
+ *                        bounded; if one ever runs out, the kernel ORs a
+ *                        nonzero code into 32-bit word 1 (byte offset 4) of
+ *                        the workspace and that call's y and state_out are
+ *                        invalid (1: a look-back wait ran out; 2: more
+ *                        tickets than workgroups, i.e. a workspace that was
+ *                        not zero-filled).  The word is sticky: the library
+ *                        never clears it, so a caller reads it after
+ *                        synchronising (one read covers every call since it
+ *                        was last cleared) and zeroes it itself.
  *   stream               HIP stream to enqueue on.
  * y must not overlap any input.  Results do not depend on Lc beyond rounding.
  */

@@ -56,6 +56,20 @@ def build(force: bool = False) -> None:
         os.replace(tmp, out)
 
 
+def build_native(out_dir: str = None) -> str:
+    """Compile the float32 build with -O3 -march=native for the host it runs on (the CPU
+    timing baseline; the parity oracle stays the portable float64 build).  Returns its path."""
+    out_dir = out_dir or _BUILD
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libessh_oracle_f32_native.so")
+    tmp = f"{out}.tmp{os.getpid()}"
+    cmd = ["gcc", "-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-DESSH_REAL=float", "-DESSH_FLOAT", "-DESSH_SUFFIX=f32", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def _bind(so_path: str, prec: str):
     lib = ctypes.CDLL(so_path)
     fn = getattr(lib, f"essh_oracle_prefill_{prec}")
@@ -129,7 +143,9 @@ prefill = make_prefill()
 prefill_f32 = make_prefill(precision="f32")
 
 
-def threads_used(precision="f64") -> int:
+def threads_used(precision="f64", so_path=None) -> int:
+    if so_path is not None:
+        return _bind(so_path, precision)[2]()
     return _lib(precision)[2]()
 
 

@@ -169,6 +169,10 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
     p.nseg = (p.nchunks + seg_chunks - 1) / seg_chunks;
     p.nblocks = p.nseq * p.nseg;
     if (p.nseg == 1) p.mode = SCAN_WHOLE;
+    // The look-back launch's eight ticket counters each own whole sequences (at
+    // most ceil(nseq / 8)); its grid gives every counter as many workgroups as
+    // the largest one has segments, the rest exit at once.
+    if (p.mode == SCAN_LOOKBACK) p.nblocks = 8 * ((p.nseq + 7) / 8) * p.nseg;
     (void)m;
     return p;
 }

@@ -339,23 +339,53 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     const int g = lane >> 4;
     const int col = lane & 15;
 
+    // Launch bookkeeping of the look-back scan (every workgroup, at its end):
+    // the last workgroup to finish re-arms the workspace header for the next
+    // launch.  The grid is a multiple of 8, so counter x has nblocks / 8
+    // workgroups.  The error word is left as it is (it stays set until the
+    // caller clears it).
+    auto finish_launch = [&]() __attribute__((always_inline)) {
+        __syncthreads();
+        if (tid == 0) {
+            // per-counter completion first, then one count per finished counter
+            const int xq = (int)(blockIdx.x & 7u);
+            const unsigned cnt = (unsigned)(plan.nblocks >> 3);
+            const unsigned done = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_DONE0 + SCAN_HDR_STRIDE * xq], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (done + 1 == cnt) {
+                const unsigned xd = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_XDONE], 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                if (xd + 1 == 8u) {   // every workgroup of this launch has finished: re-arm
+                    for (int x = 0; x < 8; ++x) {
+                        st_agent_u(&plan.hdr[SCAN_HDR_TICKET0 + SCAN_HDR_STRIDE * x], 0u);
+                        st_agent_u(&plan.hdr[SCAN_HDR_DONE0 + SCAN_HDR_STRIDE * x], 0u);
+                    }
+                    st_agent_u(&plan.hdr[SCAN_HDR_XDONE], 0u);
+                    st_agent_u(&plan.hdr[SCAN_HDR_EPOCH], sm.epoch + 1u);
+                }
+            }
+        }
+    };
+
     // ---- work item ------------------------------------------------------------------
     int seq, seg;
     unsigned tag = 0;
     if (SEG) {
-        // Tickets are taken in the order workgroups start, so every predecessor
-        // of a segment (a smaller ticket of the same counter) is already running
-        // or finished.  Eight ticket counters, one per residue of blockIdx mod 8
-        // (the XCD the hardware's round-robin dispatch sends the workgroup to),
-        // so that no single address takes every workgroup's atomic.
-        //   * nseq a multiple of 8: counter x owns the sequences
-        //     [x nseq/8, (x+1) nseq/8) and hands out their segments in
-        //     segment-major order, so one XCD reads all channels of those rows
-        //     and the clock and gate lines (channels innermost) are fetched by
-        //     one L2 only;
-        //   * otherwise counter x hands out the work items x, x + 8, x + 16, ...
-        // Either way a segment's predecessor comes from the same counter
-        // earlier, or (second form) from a smaller global ticket.
+        // Eight ticket counters, one per residue of blockIdx mod 8 (the XCD the
+        // hardware's round-robin dispatch sends the workgroup to), so that no
+        // single address takes every workgroup's atomic.  Counter x owns the
+        // whole sequences [lo_x, lo_{x+1}), lo_x = floor(x nseq / 8), and hands
+        // out their segments in segment-major order; the grid has 8 * max_x
+        // (items of counter x) workgroups, and a workgroup whose ticket is past
+        // its counter's items has nothing to do.  One XCD thus reads all
+        // channels of its sequences, whose clock and gate lines (channels
+        // innermost) are fetched by one L2.
+        // Forward progress: a segment waits only for earlier segments of its own
+        // sequence, which its own counter handed out before it, i.e. to
+        // workgroups that started before it and are running or finished.  Every
+        // wait is therefore on a resident workgroup with a smaller ticket of the
+        // same counter, whatever the order in which the hardware starts
+        // workgroups.
         const int xq = (int)(blockIdx.x & 7u);
         if (tid == 0) {
             const unsigned ep = ld_agent_u(&plan.hdr[SCAN_HDR_EPOCH]);
@@ -367,22 +397,21 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         __syncthreads();
         const int tloc = sm.ticket;
         tag = ((sm.epoch + 1u) & 0x3FFFFFFFu) << 2;
-        const bool xcd_rows = (plan.nseq & 7) == 0;
-        const int nsx = plan.nseq >> 3;
-        const int ticket = xcd_rows ? tloc : tloc * 8 + xq;
-        if (ticket >= (xcd_rows ? plan.nblocks >> 3 : plan.nblocks)) {
-            // Only possible with a workspace that was not zero-filled before first use.
+        const int lo = (int)(((long long)xq * plan.nseq) >> 3);
+        const int nsx = (int)((((long long)xq + 1) * plan.nseq) >> 3) - lo;   // sequences of counter xq
+        if (tloc >= (plan.nblocks >> 3)) {
+            // More tickets than workgroups of this residue: only possible with a
+            // workspace that was not zero-filled before first use.
             if (tid == 0) __hip_atomic_fetch_or(&plan.hdr[SCAN_HDR_ERROR], SCAN_ERR_TICKET, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
-        if (xcd_rows) {
-            seg = tloc / nsx;
-            seq = xq * nsx + (tloc - seg * nsx);
-        } else {
-            seg = ticket / plan.nseq;
-            seq = ticket - seg * plan.nseq;
+        if (tloc >= nsx * plan.nseg) {   // padding workgroup: only the completion count
+            finish_launch();
+            return;
         }
+        seg = tloc / nsx;
+        seq = lo + (tloc - seg * nsx);
     } else {
         // segment-major order: neighbouring work items are neighbouring channels
         // of one batch row over the same positions
@@ -938,6 +967,17 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     auto hi4 = [&](const f32x4_t& x) __attribute__((always_inline)) -> uint2 {
         return make_uint2(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]));
     };
+    // The bf16 rounding of what x - (its bf16 rounding h) leaves: x = h + lo4(x, h) to about
+    // 16 mantissa bits.  Feeding both halves to an MFMA keeps an fp32-class product.
+    auto lo4 = [&](const f32x4_t& x, uint2 h) __attribute__((always_inline)) -> uint2 {
+        return make_uint2(pk_bf16(x[0] - lo_f32(h.x), x[1] - hi_f32(h.x)),
+                          pk_bf16(x[2] - lo_f32(h.y), x[3] - hi_f32(h.y)));
+    };
+    // b(s) v(s) of one fragment (four positions of one column) in fp32
+    auto bv_f32 = [&](const float4& b4, uint2 vf) __attribute__((always_inline)) -> f32x4_t {
+        return f32x4_t{b4.x * lo_f32(vf.x), b4.y * hi_f32(vf.x), b4.z * lo_f32(vf.y), b4.w * hi_f32(vf.y)};
+    };
+    const uint2 zero2 = make_uint2(0u, 0u);
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
@@ -951,29 +991,37 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         float lam[4];   // Lambda_T for modes 2g, 2g+1
         if (bk.y == 0.f) {
             // factored path: scale v by b(s), constant operands.  b(s) v(s) is
-            // rounded to bf16 once and feeds both products; the state operand
-            // carries its hi and lo halves, so the state product is exact up to
-            // that one rounding of b(s) v(s).
+            // split into a bf16 hi half, which feeds the output product, and a bf16
+            // lo half; the state product takes both halves against the hi and lo
+            // halves of the lambda powers, and the carry term takes the hi and lo
+            // halves of the state, so both state-side contractions keep fp32-class
+            // precision.
             const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
-            uint2 bv[NTW];
+            uint2 bv[NTW], bvl[NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                bv[nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr[nt].x), b4.y * hi_f32(vfr[nt].x)),
-                                    pk_bf16(b4.z * lo_f32(vfr[nt].y), b4.w * hi_f32(vfr[nt].y)));
+            for (int nt = 0; nt < NTW; ++nt) {
+                const f32x4_t f = bv_f32(b4, vfr[nt]);
+                bv[nt] = hi4(f);
+                bvl[nt] = lo4(f, bv[nt]);
+            }
             if (out) {
                 const float sc = sgp->ag[T0 + col];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bf16x8_of(bv[nt], hi4(st[nt])), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    const uint2 hh = hi4(st[nt]);
+                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(bv[nt], hh), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), yD[0], acc, 0,
+                                                                  0, 0);
                     stage_y(T, nt, acc, sc);
                 }
             }
             const float at = bk.x;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
-                                                                          f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
+                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bvl[nt], bvl[nt]), mv, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
                     const float lr = l16[i], li = l16[i + 1];
@@ -1021,8 +1069,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                                                   make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) {
-                        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        const uint2 hh = hi4(st[nt]);
+                        f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0,
+                                                                      0, 0);
                         stage_y(T, nt, acc, 1.f);
                     }
                 }
@@ -1102,8 +1153,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                                                   make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) {
-                        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        const uint2 hh = hi4(st[nt]);
+                        f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0,
+                                                                      0, 0);
                         stage_y(T, nt, acc, 1.f);
                     }
                 }
@@ -1186,8 +1240,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 const float sc = bf16_to_f32((uint16_t)sgp->gr[t]);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bf16x8_of(vfr[nt], hi4(st[nt])), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    const uint2 hh = hi4(st[nt]);
+                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0, 0,
+                                                                  0);
                     stage_y(T, nt, acc, sc);
                 }
             }
@@ -1248,12 +1305,14 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     auto block_fast = [&](f32x4_t (&st)[NTW], int Bi, bool out, bool wb,
                           float (&tr)[4]) __attribute__((always_inline)) {
         const float4 bk = sgp->blkB[Bi];
-        uint2 hh[NTW];
+        uint2 hh[NTW], hl[NTW];
         if (out) {
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                hh[nt] = make_uint2(pk_bf16(st[nt][0] * bk.x, st[nt][1] * bk.x),
-                                    pk_bf16(st[nt][2] * bk.x, st[nt][3] * bk.x));
+            for (int nt = 0; nt < NTW; ++nt) {
+                const f32x4_t hs = st[nt] * bk.x;
+                hh[nt] = hi4(hs);
+                hl[nt] = lo4(hs, hh[nt]);
+            }
         }
         f32x4_t mv[NTW];
 #pragma unroll
@@ -1266,12 +1325,13 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const uint2 vfr = load_vfrag(T, nt);
-                bvh[aa][nt] = make_uint2(pk_bf16(b4.x * lo_f32(vfr.x), b4.y * hi_f32(vfr.x)),
-                                         pk_bf16(b4.z * lo_f32(vfr.y), b4.w * hi_f32(vfr.y)));
+                const f32x4_t f = bv_f32(b4, load_vfrag(T, nt));
+                bvh[aa][nt] = hi4(f);
+                const uint2 bvl = lo4(f, bvh[aa][nt]);
                 if (wb) store_bv(T, nt, bvh[aa][nt]);
                 mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bvh[aa][nt], bvh[aa][nt]), mv[nt],
                                                                  0, 0, 0);
+                mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lpA[aa], bf16x8_of(bvl, bvl), mv[nt], 0, 0, 0);
             }
             if (out) {
                 const float sc = sgp->ag[T0 + col];
@@ -1279,6 +1339,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 for (int nt = 0; nt < NTW; ++nt) {
                     f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
                                                                          f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, hl[nt]), yD[aa], acc, 0, 0, 0);
                     if (aa >= 1)
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2),
@@ -1316,10 +1377,13 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // fragments are the ones the first sweep wrote back into the tile.
     auto block_out = [&](const f32x4_t (&h)[NTW], int Bi) __attribute__((always_inline)) {
         const float4 bk = sgp->blkB[Bi];
-        uint2 hh[NTW];
+        uint2 hh[NTW], hl[NTW];
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-            hh[nt] = make_uint2(pk_bf16(h[nt][0] * bk.x, h[nt][1] * bk.x), pk_bf16(h[nt][2] * bk.x, h[nt][3] * bk.x));
+        for (int nt = 0; nt < NTW; ++nt) {
+            const f32x4_t hs = h[nt] * bk.x;
+            hh[nt] = hi4(hs);
+            hl[nt] = lo4(hs, hh[nt]);
+        }
         uint2 bvh[NB][NTW];
         const uint2 z2 = make_uint2(0u, 0u);
 #pragma unroll
@@ -1332,6 +1396,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int nt = 0; nt < NTW; ++nt) {
                 f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
                                                                      f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, hl[nt]), yD[aa], acc, 0, 0, 0);
                 if (aa >= 1)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2), yB12,
@@ -1745,30 +1810,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     }
 
-    // ---- launch bookkeeping: the last workgroup to finish re-arms the workspace -----------
-    if (SEG) {
-        __syncthreads();
-        if (tid == 0) {
-            // per-counter completion first, then one count per finished counter
-            const int xq = (int)(blockIdx.x & 7u);
-            const unsigned cnt = (unsigned)((plan.nblocks - xq + 7) / 8);
-            const unsigned done = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_DONE0 + SCAN_HDR_STRIDE * xq], 1u,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (done + 1 == cnt) {
-                const unsigned nq = (unsigned)(plan.nblocks < 8 ? plan.nblocks : 8);
-                const unsigned xd = __hip_atomic_fetch_add(&plan.hdr[SCAN_HDR_XDONE], 1u, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-                if (xd + 1 == nq) {   // every workgroup of this launch has finished: re-arm
-                    for (int x = 0; x < 8; ++x) {
-                        st_agent_u(&plan.hdr[SCAN_HDR_TICKET0 + SCAN_HDR_STRIDE * x], 0u);
-                        st_agent_u(&plan.hdr[SCAN_HDR_DONE0 + SCAN_HDR_STRIDE * x], 0u);
-                    }
-                    st_agent_u(&plan.hdr[SCAN_HDR_XDONE], 0u);
-                    st_agent_u(&plan.hdr[SCAN_HDR_EPOCH], sm.epoch + 1u);
-                }
-            }
-        }
-    }
+    if (SEG) finish_launch();
 }
 
 }  // namespace

@@ -36,6 +36,20 @@ class EsshError(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} ({status})")
 
 
+class EsshScanError(RuntimeError):
+    """A segmented prefill reported an error in its workspace (header word 1): that call's
+    outputs are invalid.  Bit 1: a bounded look-back wait ran out; bit 2: more tickets than
+    workgroups (a workspace that was not zero-filled before its first use)."""
+
+    def __init__(self, bits: int):
+        self.bits = bits
+        super().__init__(f"segmented prefill scan error bits 0x{bits:x} (outputs of that call are invalid)")
+
+
+# Byte offset and size of the error word in a prefill workspace (include/essh.h).
+SCAN_ERROR_OFFSET = 4
+
+
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("m", ctypes.c_int32), ("P", ctypes.c_int32), ("K_T", ctypes.c_int32),
@@ -169,10 +183,33 @@ class Prefill:
         _check(st, "essh_mixer_prefill")
         return self.y, self.state_out
 
+    def check(self):
+        """Synchronise and raise EsshScanError if any call so far set the workspace error word.
+
+        The word is sticky (the library never clears it), so one check after a batch of
+        calls covers all of them; it is cleared here after being reported."""
+        check_workspace(self.workspace)
+
+
+def check_workspace(workspace) -> None:
+    """Raise EsshScanError if the error word of a prefill workspace is set, and clear it."""
+    if workspace is None:
+        return
+    word = workspace[SCAN_ERROR_OFFSET:SCAN_ERROR_OFFSET + 4]
+    bits = int(word.view(torch.int32).item())   # synchronises with the device
+    if bits:
+        word.zero_()
+        raise EsshScanError(bits)
+
 
 def prefill(v, delta, g_w, g_r, rho, theta, c, K_T=None, Lc=0, state_in=None, want_state=True, y=None, zl=None):
-    """Chunked prefill of one mixer (zl: zero-lag coefficients or None).  Returns (y, state_out or None)."""
-    return Prefill(v, delta, g_w, g_r, rho, theta, c, K_T, Lc, state_in, want_state, y, zl=zl).run()
+    """Chunked prefill of one mixer (zl: zero-lag coefficients or None).  Returns (y, state_out or None).
+
+    Synchronises with the device when the call needed a workspace, to check its error word."""
+    call = Prefill(v, delta, g_w, g_r, rho, theta, c, K_T, Lc, state_in, want_state, y, zl=zl)
+    out = call.run()
+    call.check()
+    return out
 
 
 def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, y=None, zl=None):

@@ -29,19 +29,29 @@ def _essh():
 
 
 def run_gpu_prefill(inp, K_T, Lc=0, state_in=None, y_init=None, zl=None):
+    """One prefill call through the C ABI; the workspace error word is checked after it."""
     import torch
     essh = _essh()
     d = device_inputs(inp)
     s_in = None if state_in is None else to_dev(np.ascontiguousarray(state_in, np.float32))
     y = None if y_init is None else y_init
     zd = None if zl is None else to_dev(np.ascontiguousarray(zl, np.float32))
-    y, st = essh.prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
-                         K_T=K_T, Lc=Lc, state_in=s_in, y=y, zl=zd)
+    call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                        K_T=K_T, Lc=Lc, state_in=s_in, y=y, zl=zd)
+    y, st = call.run()
     torch.cuda.synchronize()
+    call.check()
     return y, st
 
 
-def check_prefill(name, inp, K_T, Lc=0, state_in=None, zl=None):
+# Regression bound on the prefill state of bf16-io launches, tighter than the 2e-2
+# acceptance bound: the measured state error of the chunked scan (fp32 state, bf16 MFMA
+# operands with the lambda powers and b(s) v(s) each split into two bf16 halves) is
+# about 1e-5; this catches a lost hi/lo split, which raises it past 1e-3.
+STATE_REGRESSION_BF16 = 5e-4
+
+
+def check_prefill(name, inp, K_T, Lc=0, state_in=None, zl=None, state_bound="default"):
     log(f"{name}: prefill K_T={K_T} Lc={Lc} shape={inp['v'].shape} io={inp['io']} zero-lag={zl is not None}")
     y, st = run_gpu_prefill(inp, K_T, Lc, state_in, zl=zl)
     ox = oracle_inputs(inp)
@@ -53,6 +63,10 @@ def check_prefill(name, inp, K_T, Lc=0, state_in=None, zl=None):
     log(f"{name}: y err {ey:.3e}, state err {es:.3e} (tol {tol:g})")
     assert ey <= tol, f"{name} K_T={K_T}: y error {ey:.3e} > {tol}"
     assert es <= tol, f"{name} K_T={K_T}: state error {es:.3e} > {tol}"
+    if state_bound == "default":
+        state_bound = STATE_REGRESSION_BF16 if inp["io"] == "bf16" else None
+    if state_bound is not None:
+        assert es <= state_bound, f"{name} K_T={K_T}: state error {es:.3e} above its regression bound {state_bound}"
     return ey, es
 
 
@@ -86,18 +100,23 @@ def test_prefill_reduced(name, widx, over, tiers, Lc):
 # and the single-launch look-back scan (40 sequences of 18 resident segments,
 # whose tickets give each XCD's counter a contiguous range of sequences; and 39
 # sequences, not a multiple of the eight counters, whose tickets interleave).
-SEGMENT_SCANS = [("three_launch_40_segments", dict(B=1, L=64 * 40 - 7, K=2), 2),
-                 ("lookback_18_segments", dict(B=5, L=64 * 70 + 9, K=8), 8),
-                 ("lookback_39_sequences_interleaved", dict(B=3, L=64 * 20 + 5, K=16), 13)]
+SEGMENT_SCANS = [("three_launch_40_segments", 1, dict(B=1, L=64 * 40 - 7, K=2), 2, 64),
+                 ("lookback_18_segments", 1, dict(B=5, L=64 * 70 + 9, K=8), 8, 64),
+                 ("lookback_39_sequences_uneven_counters", 1, dict(B=3, L=64 * 20 + 5, K=16), 13, 64),
+                 # 39 sequences (not a multiple of the 8 ticket counters) of 40 segments: a grid
+                 # of 1600 workgroups, more than one resident round
+                 ("lookback_39_sequences_1600_workgroups", 1, dict(B=3, L=64 * 4 * 40 - 3, K=16), 13, 64),
+                 # 256 segments per sequence: the segment scan composes 16 groups (1024 threads)
+                 ("three_launch_256_segments_16_groups", 4, dict(L=128 * 256), 6, 128)]
 
 
-@pytest.mark.parametrize("name,over,K_T", SEGMENT_SCANS, ids=[c[0] for c in SEGMENT_SCANS])
-def test_prefill_segment_scans(name, over, K_T):
-    w = I.workload(1, **over)
+@pytest.mark.parametrize("name,widx,over,K_T,Lc", SEGMENT_SCANS, ids=[c[0] for c in SEGMENT_SCANS])
+def test_prefill_segment_scans(name, widx, over, K_T, Lc):
+    w = I.workload(widx, **over)
     inp = I.make_prefill_inputs(w)
     rng = np.random.default_rng(11)
     s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
-    check_prefill(name, inp, K_T, 64, state_in=s0)
+    check_prefill(name, inp, K_T, Lc, state_in=s0)
 
 
 # The look-back scan and whole-sequence streaming at the other (P, m, Lc)
@@ -335,27 +354,48 @@ def test_prefill_empty_inputs():
 # Full workload sizes: sampled channels against the oracle
 # ---------------------------------------------------------------------------
 
-FULL = [(1, 24, [(0, 0), (3, 11), (7, 23)]),
-        (2, 32, [(0, 0), (9, 17), (15, 31)]),
-        (4, 24, [(0, 0), (0, 13), (0, 23)])]
+# Every full-size prefill workload at every tier, in the launch configuration bench.py
+# times: sampled (batch row, channel) sequences against the oracle, y and final state;
+# the first and the last retained channel are always among them.
+FULL = [(widx, kt) for widx in (1, 2, 4) for kt in I.WORKLOADS[widx].tiers]
+_FULL_INPUTS = {}
 
 
-@pytest.mark.parametrize("widx,K_T,samples", FULL, ids=["mixer370m_full", "mixer1p5b_full", "dna128k_full"])
-def test_prefill_full_size_sampled(widx, K_T, samples):
-    w = I.workload(widx)
-    inp = I.make_prefill_inputs(w)
+def _full_inputs(widx):
+    if widx not in _FULL_INPUTS:
+        _FULL_INPUTS.clear()
+        w = I.workload(widx)
+        inp = I.make_prefill_inputs(w)
+        _FULL_INPUTS[widx] = (w, inp, device_inputs(inp))
+    return _FULL_INPUTS[widx]
+
+
+@pytest.mark.parametrize("widx,K_T", FULL, ids=[f"{I.WORKLOADS[wi].name}_KT{kt}" for wi, kt in FULL])
+def test_prefill_full_size_sampled(widx, K_T):
+    import torch
+    essh = _essh()
+    w, inp, d = _full_inputs(widx)
     log(f"full size workload {w.name}: GPU prefill K_T={K_T} Lc={w.Lc}")
-    y, st = run_gpu_prefill(inp, K_T, w.Lc)
+    y0 = torch.full_like(d["v"], 3.0)
+    call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                        K_T=K_T, Lc=w.Lc, y=y0)
+    y, st = call.run()
+    torch.cuda.synchronize()
+    call.check()
+    assert torch.all(y[:, :, K_T:] == 3.0), "channels past the tier were written"
+    rng = np.random.default_rng(1000 + 10 * widx + K_T)
+    samples = {(0, 0), (w.B - 1, K_T - 1), (int(rng.integers(w.B)), int(rng.integers(K_T)))}
     tol = TOL[inp["io"]]
-    for b, k in samples:
+    for b, k in sorted(samples):
         sl = {key: (inp[key][b:b + 1, :, k:k + 1] if key in ("v", "delta", "g_w", "g_r") else
                     inp[key][k:k + 1] if key in ("rho", "theta", "c") else inp[key]) for key in inp}
         y_ref, s_ref = oracle.prefill(**oracle_inputs(sl))
         yk = to_host_f64(y[b:b + 1, :, k:k + 1])
         sk = to_host_f64(st[b:b + 1, k:k + 1])
         ey, es = block_err(yk, y_ref, 2), block_err(sk, s_ref, 1)
-        log(f"  (b={b}, k={k}): y err {ey:.3e}, state err {es:.3e}")
+        log(f"  (b={b}, k={k}) L={w.L}: y err {ey:.3e}, state err {es:.3e}")
         assert ey <= tol and es <= tol
+        assert es <= STATE_REGRESSION_BF16, f"state error {es:.3e} above its regression bound"
 
 
 # ---------------------------------------------------------------------------
@@ -425,9 +465,9 @@ def test_decode_iterated_equals_prefill():
     assert block_err(to_host_f64(y_dec), y_ref, 2) <= TOL["bf16"]
     assert block_err(to_host_f64(st[0]), s_ref, 1) <= 1e-5     # fp32 recurrence on both sides
     assert block_err(to_host_f64(y_dec), to_host_f64(y_pf), 2) <= TOL["bf16"]
-    # the chunked scan rounds b(s) v(s) to bf16 once before its state product, so
-    # its state meets the bf16-io bound, not the fp32 one of the decode recurrence
-    assert block_err(to_host_f64(s_pf), to_host_f64(st[0]), 1) <= TOL["bf16"]
+    # both carry an fp32-class state: decode an fp32 recurrence, the chunked scan bf16 MFMA
+    # operands split into hi and lo halves on both sides of its state contractions
+    assert block_err(to_host_f64(s_pf), to_host_f64(st[0]), 1) <= 1e-4
 
 
 def test_decode_after_prefill_full_shape_sampled():
@@ -465,3 +505,106 @@ def test_decode_after_prefill_full_shape_sampled():
         es = block_err(to_host_f64(state[l, :, k:k + 1]), s_ref, 1)
         log(f"  layer {l} channel {k}: y err {ey:.3e}, state err {es:.3e}")
         assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_decode_workload_stated_shape_all_tiers():
+    """The decode workload at its stated shape: 24 layers x (K=32, m=8, P=128), B=1, the state
+    pre-filled by a 2048-token seeded prefill per layer, then 1024 decode steps at each tier
+    K_T = 8, 16, 24, 32.  Sampled (layer, channel) pairs, the last retained channel among them,
+    are checked against the oracle run over context + steps; y of channels past the tier is
+    never written and their state keeps its prefilled value."""
+    import torch
+    essh = _essh()
+    w = I.workload(3)
+    context, steps = w.L, w.steps
+    dec = I.make_decode_inputs(w)
+    NL = w.layers
+    log(f"decode workload: {NL} layers, context {context}, {steps} steps, tiers {w.tiers}")
+    rho, theta, c = to_dev(dec["rho"]), to_dev(dec["theta"]), to_dev(dec["c"])
+    filled = torch.zeros((NL, 1, w.K, w.m, 2, w.P), device="cuda")
+    for l in range(NL):
+        _, st = essh.prefill(to_dev(dec["ctx_v"][l]), to_dev(dec["ctx_delta"][l]), to_dev(dec["ctx_g_w"][l]),
+                             to_dev(dec["ctx_g_r"][l]), rho[l], theta[l], c[l], Lc=64)
+        filled[l] = st
+    sv, sd, sgw, sgr = (to_dev(dec[k]) for k in ("step_v", "step_delta", "step_g_w", "step_g_r"))
+    dims = essh.make_dims(1, 1, w.K, w.m, w.P, w.K, 0, False, "bf16")
+    for K_T in w.tiers:
+        dims.K_T = K_T
+        state = filled.clone()
+        ys = torch.full((steps, NL, 1, w.K, w.P), 3.0, dtype=torch.bfloat16, device="cuda")
+        for s in range(steps):
+            rc = essh.essh_mixer_decode_step(NL, dims, sv[s], sd[s], sgw[s], sgr[s], rho, theta, c, None,
+                                             state, ys[s])
+            assert rc == 0
+        torch.cuda.synchronize()
+        assert torch.all(ys[:, :, :, K_T:] == 3.0), "y of channels past the tier was written"
+        assert torch.equal(state[:, :, K_T:], filled[:, :, K_T:]), "state past the tier changed"
+        for l, k in ((0, 0), (NL // 2, K_T // 2), (NL - 1, K_T - 1)):
+            seq = lambda a, b: np.concatenate([a[l][:, :, k:k + 1], np.moveaxis(b[:, l], 0, 1)[:, :, k:k + 1]],
+                                              axis=1)
+            ox = dict(v=I.as_f64(seq(dec["ctx_v"], dec["step_v"]), "bf16"),
+                      delta=seq(dec["ctx_delta"], dec["step_delta"]).astype(np.float64),
+                      g_w=I.as_f64(seq(dec["ctx_g_w"], dec["step_g_w"]), "bf16"),
+                      g_r=I.as_f64(seq(dec["ctx_g_r"], dec["step_g_r"]), "bf16"),
+                      rho=dec["rho"][l][k:k + 1].astype(np.float64),
+                      theta=dec["theta"][l][k:k + 1].astype(np.float64),
+                      c=dec["c"][l][k:k + 1].astype(np.float64))
+            y_ref, s_ref = oracle.prefill(**ox)
+            y_dec = to_host_f64(ys[:, l, :, k:k + 1]).transpose(1, 0, 2, 3)    # [1, steps, 1, P]
+            ey = block_err(y_dec, y_ref[:, context:], 2)
+            es = block_err(to_host_f64(state[l, :, k:k + 1]), s_ref, 1)
+            log(f"  K_T={K_T} layer {l} channel {k}: y err {ey:.3e}, state err {es:.3e}")
+            assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_state_init_zero_fills_every_layer_and_channel():
+    """essh_state_init writes H(0) = 0 over the whole [n_layers, B, K, m, 2, P] state."""
+    import torch
+    essh = _essh()
+    for NL, B, K, m, P in ((24, 1, 32, 8, 128), (3, 2, 5, 4, 64), (1, 3, 2, 1, 16)):
+        state = torch.full((NL, B, K, m, 2, P), float("nan"), device="cuda")
+        guard = torch.full((1024,), 7.0, device="cuda")
+        dims = essh.make_dims(B, 1, K, m, P, max(1, K // 2))
+        log(f"state_init NL={NL} B={B} K={K} m={m} P={P}")
+        essh.essh_state_init(state, NL, dims)
+        torch.cuda.synchronize()
+        assert torch.all(state == 0.0)
+        assert torch.all(guard == 7.0)
+
+
+GATES_2SIGMA = [("lookback", 1, dict(B=5, L=64 * 9 + 5, K=8), 8, 64),
+                ("whole_seq", 1, dict(B=16, L=200, K=24), 24, 64),
+                ("three_launch", 4, dict(L=1500), 6, 128),
+                ("sequential_f32", 0, {}, 8, 0),
+                ("per_mode", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
+
+
+@pytest.mark.parametrize("name,widx,over,K_T,Lc", GATES_2SIGMA, ids=[c[0] for c in GATES_2SIGMA])
+def test_prefill_gates_in_zero_two(name, widx, over, K_T, Lc):
+    """The paper's gates are eta = 2 sigma(.) in (0, 2) (App. C.2); the kernels take them as data.
+    Doubling the drawn gates is exact in bf16 and fp32."""
+    over = dict(over)
+    per_mode = over.pop("per_mode", False)
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w, per_mode=per_mode)
+    for key in ("g_w", "g_r"):
+        g = inp[key]
+        inp[key] = (g + np.uint16(0x80)) if g.dtype == np.uint16 else g * np.float32(2.0)   # bf16: exponent + 1
+    assert I.as_f64(inp["g_w"], inp["io"]).max() > 1.0
+    check_prefill("gates_2sigma_" + name, inp, K_T, Lc)
+
+
+def test_decode_gates_in_zero_two():
+    import torch
+    essh = _essh()
+    inp, state = _decode_case(2, 1, 5, 4, 64, "bf16", seed=13)
+    for key in ("g_w", "g_r"):
+        inp[key] = inp[key] + np.uint16(0x80)
+    d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
+    st = to_dev(state.copy())
+    y = essh.decode_step(st, d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], K_T=5)
+    torch.cuda.synchronize()
+    ox = {k: I.as_f64(inp[k], "bf16") for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c")}
+    y_ref, s_ref = oracle.decode_step(state.astype(np.float64), **ox, K_T=5)
+    assert block_err(to_host_f64(y).reshape(-1, 5, 64), y_ref.reshape(-1, 5, 64), 1) <= TOL["bf16"]
+    assert block_err(to_host_f64(st).reshape(-1, 5, 4 * 2 * 64), s_ref.reshape(-1, 5, 4 * 2 * 64), 1) <= 1e-5
