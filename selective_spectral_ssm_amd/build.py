@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libessh.so")
-SOURCES = ["essh_api.hip", "prefill_seq.hip", "prefill_chunk.hip", "prefill_chunk_pm.hip", "decode.hip"]
+SOURCES = ["essh_api.hip", "prefill_seq.hip", "prefill_chunk.hip", "prefill_chunk_pm.hip", "prefill_wave.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

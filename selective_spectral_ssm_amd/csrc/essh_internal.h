@@ -82,6 +82,10 @@ struct DecodeArgs {
 //   lam   [nseq * nseg][2m]         segment transfer Lambda_j (re, im)
 //   agg   [nseq * nseg][2m][P]      end state reached from a zero entering state
 //   incl  [nseq * nseg][2m][P]      true end state
+// The one-wave-per-segment kernel (wave = 1) always has the header, and after the
+// arrays above its channel-major controls:
+//   cdl   [nseq][L]                 clock delta of sequence b K_T + k
+//   cgg   [nseq][L]                 write gate bits | read gate bits << 16
 // The header must be zero before the first launch that uses the workspace;
 // each launch leaves it re-armed for the next one.
 enum {
@@ -106,12 +110,16 @@ enum { SCAN_WHOLE = 0, SCAN_LOOKBACK = 1, SCAN_SPLIT = 2 };
 
 struct ScanPlan {
     int mode;
+    int wave;                 // 1: the one-wave-per-segment kernel (prefill_wave.hip)
+    int L;
     int nseq, nchunks, seg_chunks, nseg, nblocks;
     unsigned* hdr;
     unsigned* flags;
     float* lam;
     float* agg;
     float* incl;
+    float* cdl;
+    uint32_t* cgg;
 };
 
 // Launchers (host side).  Each returns hipSuccess or the launch error.
@@ -122,6 +130,8 @@ size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc, int 
 void bind_workspace(ScanPlan& plan, void* workspace, int m, int P);
 hipError_t launch_prefill_chunked(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s);
 hipError_t launch_prefill_chunked_pm(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s);
+bool wave_supported(int m, int P, int Lc, int io_dtype, int per_mode);
+hipError_t launch_prefill_wave(const PrefillArgs& a, int m, const ScanPlan& plan, hipStream_t s);
 hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);

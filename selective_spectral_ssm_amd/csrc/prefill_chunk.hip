@@ -128,9 +128,32 @@ bool chunked_supported(int m, int P, int Lc, int io_dtype, int per_mode) {
 
 ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode) {
     ScanPlan p{};
+    p.L = L;
     p.nseq = B * K_T;
     p.nchunks = (L + Lc - 1) / Lc;
     if (p.nseq == 0 || p.nchunks == 0) return p;
+    constexpr int SPLIT_MAX_SEQ = 32;
+    if (p.nseq <= SPLIT_MAX_SEQ && wave_supported(m, P, Lc, ESSH_BF16, per_mode)) {
+        // Few, long sequences with P = 64: the three-launch scan over about WAVE_TARGET
+        // segments with one wave per (sequence, segment) (prefill_wave.hip).
+        constexpr int WAVE_TARGET = 3072;
+        p.wave = 1;
+        int seg_chunks = p.nchunks;
+        p.mode = SCAN_SPLIT;
+        {
+            const long long want = ((long long)p.nchunks * p.nseq + WAVE_TARGET - 1) / WAVE_TARGET;
+            const int max_seg = 1 + SCAN_PER * (1024 / P);
+            const int min_chunks = (p.nchunks + max_seg - 1) / max_seg;
+            seg_chunks = (int)(want > min_chunks ? want : min_chunks);
+        }
+        if (seg_chunks < 1) seg_chunks = 1;
+        if (seg_chunks > p.nchunks) seg_chunks = p.nchunks;
+        p.seg_chunks = seg_chunks;
+        p.nseg = (p.nchunks + seg_chunks - 1) / seg_chunks;
+        p.nblocks = p.nseq * p.nseg;
+        if (p.nseg == 1) p.mode = SCAN_WHOLE;
+        return p;
+    }
     // With about 1.5 sequences per CU or more (one per CU when P = 128), whole
     // sequences keep the GPU busy.  Below that, sequences are cut into segments of as many chunks as
     // a workgroup keeps resident in LDS, and a look-back scan links them.
@@ -145,7 +168,6 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
     // in 80 us against 51; P = 64 keeps the look-back at 192 sequences (41 us
     // against 63).
     const int SEQ_ENOUGH = P >= 128 ? 256 : 384;
-    constexpr int SPLIT_MAX_SEQ = 32;
     constexpr int SPLIT_TARGET = 1536;
     int seg_chunks = p.nchunks;
     p.mode = SCAN_WHOLE;
@@ -177,32 +199,65 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
     return p;
 }
 
-size_t lookback_bytes(const ScanPlan& p, int m, int P) {
-    if (p.nseg <= 1) return 0;
-    const size_t slots = (size_t)p.nseq * p.nseg;
-    return align256(SCAN_HDR_WORDS * sizeof(unsigned)) + align256(slots * sizeof(unsigned)) +
-           align256(slots * 2 * m * sizeof(float)) + 2 * align256(slots * 2 * (size_t)m * P * sizeof(float));
+// Byte offsets of the workspace arrays (see ScanPlan); an array that the plan does not use
+// has none.
+struct WsLayout {
+    size_t hdr, flags, lam, agg, incl, cdl, cgg, total;
+    bool has_hdr, has_scan, has_ctrl;
+};
+
+WsLayout ws_layout(const ScanPlan& p, int m, int P) {
+    WsLayout w{};
+    w.has_scan = p.nseg > 1;
+    w.has_ctrl = p.wave != 0;
+    w.has_hdr = w.has_scan || w.has_ctrl;
+    size_t off = 0;
+    if (w.has_hdr) {
+        w.hdr = off;
+        off += align256(SCAN_HDR_WORDS * sizeof(unsigned));
+    }
+    if (w.has_scan) {
+        const size_t slots = (size_t)p.nseq * p.nseg;
+        w.flags = off;
+        off += align256(slots * sizeof(unsigned));
+        w.lam = off;
+        off += align256(slots * 2 * m * sizeof(float));
+        w.agg = off;
+        off += align256(slots * 2 * (size_t)m * P * sizeof(float));
+        w.incl = off;
+        off += align256(slots * 2 * (size_t)m * P * sizeof(float));
+    }
+    if (w.has_ctrl) {
+        const size_t n = (size_t)p.nseq * p.L;
+        w.cdl = off;
+        off += align256(n * sizeof(float));
+        w.cgg = off;
+        off += align256(n * sizeof(uint32_t));
+    }
+    w.total = off;
+    return w;
 }
 
 size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc, int per_mode) {
     const ScanPlan p = plan_chunked(B, L, K_T, m, P, Lc, per_mode);
     if (p.nblocks == 0) return 0;
-    return lookback_bytes(p, m, P);
+    return ws_layout(p, m, P).total;
 }
 
 void bind_workspace(ScanPlan& p, void* ws, int m, int P) {
-    if (p.nseg <= 1) return;
-    const size_t slots = (size_t)p.nseq * p.nseg;
+    const WsLayout w = ws_layout(p, m, P);
     char* base = static_cast<char*>(ws);
-    p.hdr = reinterpret_cast<unsigned*>(base);
-    base += align256(SCAN_HDR_WORDS * sizeof(unsigned));
-    p.flags = reinterpret_cast<unsigned*>(base);
-    base += align256(slots * sizeof(unsigned));
-    p.lam = reinterpret_cast<float*>(base);
-    base += align256(slots * 2 * m * sizeof(float));
-    p.agg = reinterpret_cast<float*>(base);
-    base += align256(slots * 2 * (size_t)m * P * sizeof(float));
-    p.incl = reinterpret_cast<float*>(base);
+    if (w.has_hdr) p.hdr = reinterpret_cast<unsigned*>(base + w.hdr);
+    if (w.has_scan) {
+        p.flags = reinterpret_cast<unsigned*>(base + w.flags);
+        p.lam = reinterpret_cast<float*>(base + w.lam);
+        p.agg = reinterpret_cast<float*>(base + w.agg);
+        p.incl = reinterpret_cast<float*>(base + w.incl);
+    }
+    if (w.has_ctrl) {
+        p.cdl = reinterpret_cast<float*>(base + w.cdl);
+        p.cgg = reinterpret_cast<uint32_t*>(base + w.cgg);
+    }
 }
 
 hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s) {
@@ -214,6 +269,7 @@ hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s) {
 
 hipError_t launch_prefill_chunked(const PrefillArgs& a, int m, int P, const ScanPlan& plan, hipStream_t s) {
     if (a.per_mode) return launch_prefill_chunked_pm(a, m, P, plan, s);
+    if (plan.wave) return launch_prefill_wave(a, m, plan, s);
     switch (P) {
         case 16: return launch_m<16>(a, m, plan, s);
         case 32: return launch_m<32>(a, m, plan, s);

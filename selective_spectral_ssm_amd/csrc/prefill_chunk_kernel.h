@@ -104,6 +104,9 @@ constexpr unsigned FLAG_INCL = 2u;   // inclusive state (true state after the se
 // plus a short sleep, so this is tens of milliseconds); exceeding it records
 // SCAN_ERR_TIMEOUT in the workspace header instead of waiting forever.
 constexpr int SPIN_LIMIT = 1 << 16;
+// Predecessor records a look-back reads per memory round trip (independent loads, then folded
+// in order).
+constexpr int LB_BATCH = 2;
 // s_waitcnt operand: vector memory counter 0, the other counters unconstrained.
 constexpr int WAIT_VMEM0 = 0x0F70;
 
@@ -1535,10 +1538,10 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const int cnt = sm.lb_cnt;
             const bool found = sm.lb_found != 0;
             __syncthreads();   // sm.lb_* may be rewritten by the next window
-            for (int l0 = 0; l0 < cnt; l0 += 2) {
-                float sv[2][NTW][4], lv[2][4];
+            for (int l0 = 0; l0 < cnt; l0 += LB_BATCH) {
+                float sv[LB_BATCH][NTW][4], lv[LB_BATCH][4];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < LB_BATCH; ++u) {
                     const int l = l0 + u;
                     if (l >= cnt) break;
                     const int pred = hi - l;
@@ -1560,7 +1563,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < LB_BATCH; ++u) {
                     if (l0 + u >= cnt) break;
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) {

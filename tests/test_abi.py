@@ -122,12 +122,14 @@ def _call_ws(dims, ws, ws_bytes):
 
 def test_segmented_prefill_needs_a_workspace(lib):
     """Few (batch row, channel) sequences -> the scan is segmented and needs look-back space:
-    at least the aggregate and inclusive states (2 x 2m x P fp32) of every segment."""
+    at least the aggregate and inclusive states (2 x 2m x P fp32) of every segment, and at most
+    that for one segment per chunk plus a channel-major copy of the controls (8 bytes per
+    position and sequence)."""
     d = essh.make_dims(1, 131072, 24, 4, 64, 6, 128)
     need = essh.essh_prefill_workspace_bytes(d)
     nchunks = 131072 // 128
     assert need >= 2 * (1 * 6) * 2 * 2 * 4 * 64 * 4          # at least two segments per sequence
-    assert need <= 2 * (1 * 6) * nchunks * 2 * 4 * 64 * 4 + 2 * 6 * nchunks * 64 + 4096
+    assert need <= 2 * (1 * 6) * nchunks * 2 * 4 * 64 * 4 + 2 * 6 * nchunks * 64 + 6 * 131072 * 8 + 4096
     assert _call_ws(d, None, 0) == essh.ESSH_ERR_WORKSPACE
     assert _call_ws(d, FAKE * 16, need - 1) == essh.ESSH_ERR_WORKSPACE
     assert _call_ws(d, FAKE * 16 + 16, need) == essh.ESSH_ERR_WORKSPACE     # not 256-byte aligned
