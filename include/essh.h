@@ -62,8 +62,12 @@ typedef enum {
     ESSH_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, K_T outside [1, K] */
     ESSH_ERR_UNSUPPORTED = -2,   /* m, P, Lc or dtype outside the compiled set */
     ESSH_ERR_WORKSPACE = -3,     /* workspace missing or smaller than essh_prefill_workspace_bytes() */
-    ESSH_ERR_HIP = -4            /* a HIP launch or query failed on the host side */
+    ESSH_ERR_HIP = -4,           /* a HIP launch or query failed on the host side */
+    ESSH_ERR_SCRATCH = -5        /* essh_mixer_prefill_noalloc: dims need more than its static scratch */
 } essh_status;
+
+/* Size of the static device scratch of essh_mixer_prefill_noalloc, per GPU. */
+#define ESSH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum { ESSH_F32 = 0, ESSH_BF16 = 1 } essh_dtype;
 
@@ -148,6 +152,33 @@ essh_status essh_mixer_prefill(const essh_dims* d,
                                const float* rho, const float* theta, const float* c, const float* zl,
                                const float* state_in, float* state_out, void* y,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * essh_mixer_prefill_noalloc -- essh_mixer_prefill without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * look-back records live in a static device array of
+ * ESSH_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends; the call allocates nothing.
+ *
+ * Arguments, layouts and results are those of essh_mixer_prefill, except:
+ *   scan_error           NULL, or a 4-byte-aligned device word into which the
+ *                        call ORs its scan error code (the codes of the
+ *                        workspace error word of essh_mixer_prefill), in
+ *                        stream order; the caller zeroes it.
+ * Each call clears the part of the array that must start at zero, so no
+ * earlier call's contents matter.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (several streams, or several
+ * host threads) race and give invalid results; order them.
+ * Returns ESSH_ERR_SCRATCH, before launching anything, when
+ * essh_prefill_workspace_bytes(d) exceeds ESSH_NOALLOC_SCRATCH_BYTES (for
+ * example 1 x 131072 positions at K_T = 24, m = 4, P = 64 needs about 38 MB).
+ */
+essh_status essh_mixer_prefill_noalloc(const essh_dims* d,
+                                       const void* v, const float* delta, const void* g_w, const void* g_r,
+                                       const float* rho, const float* theta, const float* c, const float* zl,
+                                       const float* state_in, float* state_out, void* y,
+                                       uint32_t* scan_error, hipStream_t stream);
 
 /*
  * essh_mixer_decode_step -- one token through n_layers independent mixers

@@ -44,6 +44,9 @@ const char* essh_status_string(essh_status s) {
         case ESSH_ERR_UNSUPPORTED: return "ESSH_ERR_UNSUPPORTED: m, P, Lc or dtype outside the compiled set";
         case ESSH_ERR_WORKSPACE: return "ESSH_ERR_WORKSPACE: workspace missing or too small";
         case ESSH_ERR_HIP: return "ESSH_ERR_HIP: a HIP launch failed";
+        case ESSH_ERR_SCRATCH:
+            return "ESSH_ERR_SCRATCH: the dims need more look-back space than the static scratch of "
+                   "essh_mixer_prefill_noalloc (ESSH_NOALLOC_SCRATCH_BYTES); use essh_mixer_prefill";
         default: return "ESSH: unknown status";
     }
 }

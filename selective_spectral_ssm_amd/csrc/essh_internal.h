@@ -133,6 +133,9 @@ hipError_t launch_prefill_chunked_pm(const PrefillArgs& a, int m, int P, const S
 bool wave_supported(int m, int P, int Lc, int io_dtype, int per_mode);
 hipError_t launch_prefill_wave(const PrefillArgs& a, int m, const ScanPlan& plan, hipStream_t s);
 hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s);
+// Leading workspace bytes that must be zero before a prefill with dims d (scan header and
+// look-back flags); 0 when the plan keeps no look-back records.
+size_t prefill_clear_bytes(const essh_dims* d);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int B, int K, int K_T, int m, int P, hipStream_t s);

@@ -238,6 +238,15 @@ WsLayout ws_layout(const ScanPlan& p, int m, int P) {
     return w;
 }
 
+size_t prefill_clear_bytes(const essh_dims* d) {
+    if (!d || essh_prefill_workspace_bytes(d) == 0) return 0;
+    const int lc = d->Lc == 0 ? 64 : d->Lc;
+    const ScanPlan p = plan_chunked(d->B, d->L, d->K_T, d->m, d->P, lc, d->ctrl_per_mode);
+    const WsLayout w = ws_layout(p, d->m, d->P);
+    if (w.has_scan) return w.lam;
+    return w.has_hdr ? align256(SCAN_HDR_WORDS * sizeof(unsigned)) : 0;
+}
+
 size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc, int per_mode) {
     const ScanPlan p = plan_chunked(B, L, K_T, m, P, Lc, per_mode);
     if (p.nblocks == 0) return 0;

@@ -19,11 +19,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libessh.so")
 
 ESSH_OK, ESSH_ERR_INVALID_ARG, ESSH_ERR_UNSUPPORTED, ESSH_ERR_WORKSPACE, ESSH_ERR_HIP = 0, -1, -2, -3, -4
+ESSH_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 ESSH_F32, ESSH_BF16 = 0, 1
 
 # Every symbol the C header declares (checked by the tests against include/essh.h).
 EXPORTED = ("essh_abi_version", "essh_status_string", "essh_state_init",
-            "essh_prefill_workspace_bytes", "essh_mixer_prefill", "essh_mixer_decode_step")
+            "essh_prefill_workspace_bytes", "essh_mixer_prefill", "essh_mixer_prefill_noalloc",
+            "essh_mixer_decode_step")
 
 
 class EsshLibraryMissing(RuntimeError):
@@ -79,6 +82,8 @@ def lib():
         L.essh_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
         L.essh_mixer_prefill.restype = ctypes.c_int
         L.essh_mixer_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12 + [SZ, P]
+        L.essh_mixer_prefill_noalloc.restype = ctypes.c_int
+        L.essh_mixer_prefill_noalloc.argtypes = [ctypes.POINTER(Dims)] + [P] * 13
         L.essh_mixer_decode_step.restype = ctypes.c_int
         L.essh_mixer_decode_step.argtypes = [I32, ctypes.POINTER(Dims)] + [P] * 10 + [P]
         _lib = L
@@ -140,6 +145,14 @@ def essh_mixer_prefill(dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state_
     return lib().essh_mixer_prefill(ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w), _ptr(g_r),
                                     _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl), _ptr(state_in), _ptr(state_out),
                                     _ptr(y), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def essh_mixer_prefill_noalloc(dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state_in, state_out, y,
+                               scan_error=None, stream=None) -> int:
+    """Direct call of the allocation-free prefill; returns the status code."""
+    return lib().essh_mixer_prefill_noalloc(ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w), _ptr(g_r),
+                                            _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl), _ptr(state_in),
+                                            _ptr(state_out), _ptr(y), _ptr(scan_error), _stream(stream))
 
 
 def essh_mixer_decode_step(n_layers: int, dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state, y,

@@ -37,8 +37,25 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert essh.status_string(code).startswith("ESSH_")
+
+
+def test_noalloc_scratch_limit(lib):
+    """The allocation-free prefill refuses, before launching anything, dims whose look-back
+    records exceed its static scratch, and validates dims like the workspace entry point."""
+    m = re.search(r"#define\s+ESSH_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == essh.NOALLOC_SCRATCH_BYTES
+    p = [ctypes.c_void_p(FAKE)] * 7
+    big = essh.make_dims(1, 131072, 24, 4, 64, 24, 128)
+    assert essh.essh_prefill_workspace_bytes(big) > essh.NOALLOC_SCRATCH_BYTES
+    assert lib.essh_mixer_prefill_noalloc(ctypes.byref(big), *p, None, None, None, ctypes.c_void_p(FAKE),
+                                          None, None) == essh.ESSH_ERR_SCRATCH
+    bad = essh.make_dims(1, 2048, 24, 4, 64, 25, 64)   # K_T > K
+    assert lib.essh_mixer_prefill_noalloc(ctypes.byref(bad), *p, None, None, None, ctypes.c_void_p(FAKE),
+                                          None, None) == essh.ESSH_ERR_INVALID_ARG
+    fits = essh.make_dims(1, 131072, 24, 4, 64, 18, 128)
+    assert 0 < essh.essh_prefill_workspace_bytes(fits) <= essh.NOALLOC_SCRATCH_BYTES
 
 
 FAKE = 0x10000          # 16-byte-aligned stand-in address; never dereferenced on these error paths
