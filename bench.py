@@ -38,7 +38,7 @@ SLEEP_CYCLES = 200_000_000
 # per launch, and the decode kernel's median duration.  Each records the SHA-256 of the kernel
 # sources it was taken on and is used only while they still hash to it.
 PREFILL_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
-                   for f in ("prefill_chunk_kernel.h", "prefill_chunk.hip", "essh_internal.h")]
+                   for f in ("prefill_chunk_kernel.h", "prefill_chunk.hip", "prefill_wave.hip", "essh_internal.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "selective_spectral_ssm_amd", "csrc", f)
                   for f in ("decode.hip", "essh_internal.h")]
 # The headline: the largest single-GPU workload (128K-token DNA-like prefill) at its full tier.
@@ -71,8 +71,8 @@ def source_hash(files):
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 
 
-def profile_value(name, key, sources):
-    """A number recorded in profiles/<name>.md (a line "- key: `value`"), or None when the file
+def profile_text(name, key, sources):
+    """A value recorded in profiles/<name>.md (a line "- key: `value`"), or None when the file
     is missing or was taken on kernel sources that no longer hash to its source_sha256."""
     try:
         text = open(os.path.join(ROOT, "profiles", name + ".md")).read()
@@ -81,9 +81,13 @@ def profile_value(name, key, sources):
     kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
     if kv.get("source_sha256") != source_hash(sources):
         return None
+    return kv.get(key)
+
+
+def profile_value(name, key, sources):
     try:
-        return float(kv[key])
-    except (KeyError, ValueError):
+        return float(profile_text(name, key, sources))
+    except (TypeError, ValueError):
         return None
 
 
@@ -370,6 +374,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", type=int, default=HEADLINE[0],
+                    help="prefill workload of the main line (profiling runs; default: the headline)")
+    ap.add_argument("--kt", type=int, default=HEADLINE[1], help="its tier K_T")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode at every tier (profiling runs); prints the decode JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -383,14 +392,25 @@ def main():
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
 
-    widx, KT = HEADLINE
     from selective_spectral_ssm_amd import inputs as I
+    if args.decode_only:
+        out = []
+        for kt in I.WORKLOADS[3].tiers:
+            log(f"decode: 24 layers K_T={kt}")
+            out.append(decode_case(kt))
+        print(json.dumps({"decode_tiers": out}))
+        return
+    widx, KT = args.workload, args.kt
     wname = I.WORKLOADS[widx].name
     log(f"prefill: {wname} K_T={KT}")
     main_res, w, inp = prefill_case(widx, KT, args.steps, args.warmup)
     tag = f"prefill_{wname.replace('_prefill', '')}_kt{KT}"
     traffic = profile_value("hbm_traffic_" + tag, "hbm_bytes_per_launch", PREFILL_SOURCES)
     mfma = profile_value("mfma_" + tag, "mfma_flops_per_launch", PREFILL_SOURCES)
+    # the launches of one prefill call and the sum of their average durations in the
+    # committed kernel trace of this command (rocprofv3), beside the live HIP-event figure
+    launches = profile_text("kernel_trace_" + tag, "launches", PREFILL_SOURCES)
+    trace_us = profile_value("kernel_trace_" + tag, "sum_avg_us", PREFILL_SOURCES)
     copy_gbs = copy_bandwidth()
     log(f"plain copy: {copy_gbs:.0f} GB/s (read + write)")
     us = main_res["us_per_launch"]
@@ -409,7 +429,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "K": w.K, "K_T": KT, "m": w.m, "P": w.P,
                    "Lc": w.Lc, "io": w.io, "state": "fp32", "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel (every launch of one essh_mixer_prefill call)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "every launch of one essh_mixer_prefill call" + (f": {launches}" if launches else ""),
+                     "rocprof_sum_avg_us": trace_us,
                      "achieved": main_res["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": main_res["achieved_GBs"] / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic / (us * 1e-6) / 1e9,
@@ -430,7 +452,7 @@ def main():
         extra = []
         for wi in (1, 2, 4):
             for kt in I.WORKLOADS[wi].tiers:
-                if (wi, kt) == HEADLINE:
+                if (wi, kt) == (widx, KT):
                     r = main_res
                 else:
                     log(f"tier sweep: workload {wi} K_T={kt}")
