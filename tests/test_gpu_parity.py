@@ -83,6 +83,9 @@ REDUCED = [
     ("m1_p16", 1, dict(B=2, L=130, K=3, m=1, P=16), (3,), 64),
     ("m2_p32", 1, dict(B=2, L=130, K=3, m=2, P=32), (2,), 64),
     ("m8_p64", 1, dict(B=2, L=150, K=3, m=8, P=64), (3,), 64),
+    # few sequences with P = 64 take the one-wave-per-segment kernel at every m it is built for
+    ("wave_m1_p64", 1, dict(B=2, L=200, K=3, m=1), (3,), 64),
+    ("wave_m2_p64_lc128", 1, dict(B=1, L=300, K=4, m=2), (4,), 128),
     ("bf16_p128_m4", 2, dict(B=1, L=129, K=2, m=4), (2,), 64),
 ]
 
