@@ -28,10 +28,9 @@
 //   state, source sub-block a (A operand, lane (g, col) = state row (mode, re/im)):
 //     {Re, Im}(lambda^{63-s}) b(s) split into bf16 hi and lo halves, against B = [ v ; v ],
 //     so the state product is exact up to the lambda-power and b(s) rounding to ~16 bits.
-// Blocks are staged by asynchronous global-to-LDS copies into a ring of stages (8 KB of v plus
-// the block's controls each), one block ahead in the streaming role and three ahead in the
-// aggregate role (which stores nothing until its end); y is staged in place and written back
-// by whole 128-byte rows.  v is copied by whole 128-byte rows too; the controls come from a
+// Blocks are staged by asynchronous global-to-LDS copies into a ring of two stages (8 KB of v
+// plus the block's controls each), one block ahead, so that eight waves fit a CU; y is staged
+// in place and written back by whole 128-byte rows.  v is copied by whole 128-byte rows too; the controls come from a
 // channel-major copy made by a first launch (pack_ctrl_kernel), so that a block's controls
 // are two contiguous 256-byte reads instead of 64-way gathers across the channel rows.
 #include "prefill_chunk_kernel.h"
@@ -59,17 +58,18 @@ struct __align__(16) WTables {
     float4 mtab[M];               // (rho, theta, Re c, Im c)
     float mza[M];                 // zero-lag coefficients a_j
 };
-struct __align__(16) WStageV {
-    uint16_t v[WSTV];
-};
 struct __align__(16) WStageC {
     float dl[WBLK];               // clock
     uint32_t gg[WBLK];            // write gate bf16 bits | read gate bf16 bits << 16
 };
-struct __align__(16) WFactors {
-    float bq[WBLK];               // block path: b(s);  sub-block path: clock sum from the block start (log2 units)
-    float ag[WBLK];               // block path: g_r(t) a(t);  sub-block path: write gate
-    float gr[WBLK];               // sub-block path: read gate
+struct __align__(16) WStage {
+    uint16_t v[WSTV];
+    WStageC c;
+};
+struct __align__(16) WFactors {   // per-position factors of the sub-block path
+    float bq[WBLK];               // clock sum from the block start (log2 units)
+    float ag[WBLK];               // write gate
+    float gr[WBLK];               // read gate
 };
 
 // Channel-major copy of the controls of the retained channels, sequence seq = b K_T + k:
@@ -83,23 +83,63 @@ __global__ void __launch_bounds__(256) pack_ctrl_kernel(PrefillArgs a, ScanPlan 
     const int t0 = blockIdx.x * WBLK, k0 = blockIdx.y * 32, b = blockIdx.z;
     const uint16_t* gw = static_cast<const uint16_t*>(a.g_w);
     const uint16_t* gr = static_cast<const uint16_t*>(a.g_r);
-    for (int i = threadIdx.x; i < 32 * WBLK; i += 256) {
-        const int pos = i >> 5, kk = i & 31;
-        const int t = t0 + pos, k = k0 + kk;
-        if (t < a.L && k < a.K_T) {
-            const size_t row = ((size_t)b * a.L + t) * a.K + k;
-            sd[kk][pos] = a.delta[row];
-            sg[kk][pos] = (uint32_t)gw[row] | ((uint32_t)gr[row] << 16);
+    const bool vec4 = (a.K & 3) == 0 && (a.K_T & 3) == 0 && (reinterpret_cast<uintptr_t>(a.delta) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(gw) & 7) == 0 && (reinterpret_cast<uintptr_t>(gr) & 7) == 0;
+    if (vec4) {
+        // four channels per load: 16-byte clock and 8-byte gate reads (rows start at a
+        // multiple of four channels)
+        for (int i = threadIdx.x; i < 8 * WBLK; i += 256) {
+            const int pos = i >> 3, kq = 4 * (i & 7);
+            const int t = t0 + pos, k = k0 + kq;
+            if (t < a.L && k < a.K_T) {
+                const size_t row = ((size_t)b * a.L + t) * a.K + k;
+                const float4 d = *reinterpret_cast<const float4*>(a.delta + row);
+                const uint2 w = *reinterpret_cast<const uint2*>(gw + row);
+                const uint2 r = *reinterpret_cast<const uint2*>(gr + row);
+                sd[kq][pos] = d.x;
+                sd[kq + 1][pos] = d.y;
+                sd[kq + 2][pos] = d.z;
+                sd[kq + 3][pos] = d.w;
+                sg[kq][pos] = (w.x & 0xffffu) | (r.x << 16);
+                sg[kq + 1][pos] = (w.x >> 16) | (r.x & 0xffff0000u);
+                sg[kq + 2][pos] = (w.y & 0xffffu) | (r.y << 16);
+                sg[kq + 3][pos] = (w.y >> 16) | (r.y & 0xffff0000u);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < 32 * WBLK; i += 256) {
+            const int pos = i >> 5, kk = i & 31;
+            const int t = t0 + pos, k = k0 + kk;
+            if (t < a.L && k < a.K_T) {
+                const size_t row = ((size_t)b * a.L + t) * a.K + k;
+                sd[kk][pos] = a.delta[row];
+                sg[kk][pos] = (uint32_t)gw[row] | ((uint32_t)gr[row] << 16);
+            }
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 32 * WBLK; i += 256) {
-        const int kk = i >> 6, pos = i & 63;
-        const int t = t0 + pos, k = k0 + kk;
-        if (t < a.L && k < a.K_T) {
-            const size_t o = ((size_t)b * a.K_T + k) * a.L + t;
-            plan.cdl[o] = sd[kk][pos];
-            plan.cgg[o] = sg[kk][pos];
+    if ((a.L & 3) == 0) {
+        // four positions per store (a channel's row starts at a multiple of four positions)
+        for (int i = threadIdx.x; i < 32 * (WBLK / 4); i += 256) {
+            const int kk = i >> 4, pos = 4 * (i & 15);
+            const int t = t0 + pos, k = k0 + kk;
+            if (t < a.L && k < a.K_T) {   // L % 4 == 0: the four positions are all in range
+                const size_t o = ((size_t)b * a.K_T + k) * a.L + t;
+                *reinterpret_cast<float4*>(plan.cdl + o) =
+                    make_float4(sd[kk][pos], sd[kk][pos + 1], sd[kk][pos + 2], sd[kk][pos + 3]);
+                *reinterpret_cast<uint4*>(plan.cgg + o) =
+                    make_uint4(sg[kk][pos], sg[kk][pos + 1], sg[kk][pos + 2], sg[kk][pos + 3]);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < 32 * WBLK; i += 256) {
+            const int kk = i >> 6, pos = i & 63;
+            const int t = t0 + pos, k = k0 + kk;
+            if (t < a.L && k < a.K_T) {
+                const size_t o = ((size_t)b * a.K_T + k) * a.L + t;
+                plan.cdl[o] = sd[kk][pos];
+                plan.cgg[o] = sg[kk][pos];
+            }
         }
     }
 }
@@ -117,18 +157,17 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
     constexpr int ROWS = 2 * M;
     __shared__ WTables<M> tb;
     __shared__ WFactors fc;
-    // Each stage is an LDS object of its own, so the compiler orders a read of one stage
-    // only behind the asynchronous copies into that stage.
-    __shared__ WStageV sv0, sv1, sv2, sv3;
-    __shared__ WStageC sc0, sc1, sc2, sc3;
+    // Each stage (v and controls together) is an LDS object of its own: the compiler follows
+    // the asynchronous copies into LDS per object (a few objects at most), and orders a read
+    // of one stage only behind the copies into that stage.
+    __shared__ WStage st0, st1, st2, st3;
     // (a stage index past NS - 1 never occurs; the selections name only the NS stages in use,
     // so the others are not allocated even where the index is not a compile-time constant)
-    auto stv = [&](int s) __attribute__((always_inline)) -> uint16_t* {
-        return s == 0 ? sv0.v : (NS == 2 || s == 1) ? sv1.v : (NS == 3 || s == 2) ? sv2.v : sv3.v;
+    auto stg = [&](int s) __attribute__((always_inline)) -> WStage* {
+        return s == 0 ? &st0 : (NS == 2 || s == 1) ? &st1 : (NS == 3 || s == 2) ? &st2 : &st3;
     };
-    auto stc = [&](int s) __attribute__((always_inline)) -> WStageC* {
-        return s == 0 ? &sc0 : (NS == 2 || s == 1) ? &sc1 : (NS == 3 || s == 2) ? &sc2 : &sc3;
-    };
+    auto stv = [&](int s) __attribute__((always_inline)) -> uint16_t* { return stg(s)->v; };
+    auto stc = [&](int s) __attribute__((always_inline)) -> WStageC* { return &stg(s)->c; };
 
     const int lane = threadIdx.x;
     const int g = lane >> 4;
@@ -350,12 +389,16 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
         if (n == WBLK && qe2 <= SPAN2_BLOCK_MAX) {
             // ---- block path ----
             const float mid = 0.5f * qe2;
-            fc.bq[lane] = exp2f(q2 - mid) * gwv;
-            fc.ag[lane] = exp2f(mid - q2) * grv;
+            // b(s) and g_r(t) a(t) stay in registers and are read across lanes: an LDS copy of
+            // them would make the compiler wait for every copy in flight before reading it
+            const float bql = exp2f(q2 - mid) * gwv;
+            const float agl = exp2f(mid - q2) * grv;
             const float Hs = exp2f(-mid), Ae = exp2f(mid - qe2), Le = exp2f(-qe2);
             float4 bq4[4];
 #pragma unroll
-            for (int aa = 0; aa < 4; ++aa) bq4[aa] = *reinterpret_cast<const float4*>(&fc.bq[16 * aa + 4 * g]);
+            for (int aa = 0; aa < 4; ++aa)
+                bq4[aa] = make_float4(__shfl(bql, 16 * aa + 4 * g), __shfl(bql, 16 * aa + 4 * g + 1),
+                                      __shfl(bql, 16 * aa + 4 * g + 2), __shfl(bql, 16 * aa + 4 * g + 3));
             const float bqv[4][4] = {{bq4[0].x, bq4[0].y, bq4[0].z, bq4[0].w},
                                      {bq4[1].x, bq4[1].y, bq4[1].z, bq4[1].w},
                                      {bq4[2].x, bq4[2].y, bq4[2].z, bq4[2].w},
@@ -381,7 +424,7 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
                 const bf16x8_t W = bf16x8_of(wh, lo4(w, wh));
                 bf16x8_t Bd, B12, B3;
                 if constexpr (!AGG) {
-                    const float at = fc.ag[16 * aa + col];
+                    const float at = __shfl(agl, 16 * aa + col);
                     const float ah = at * Hs;
                     Bd = bf16x8_of(
                         make_uint2(pk_bf16(at * bqv[aa][0] * psv[0][0], at * bqv[aa][1] * psv[0][1]),
@@ -592,8 +635,11 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
     }
 }
 
+// The aggregate role, which stores nothing until its end, can also run a deeper ring (the
+// waits above allow it); with three or four stages its LDS halves the waves per CU, and it
+// measured 13-15% slower.
 #ifndef ESSH_WAVE_STAGES_AGG
-#define ESSH_WAVE_STAGES_AGG 4
+#define ESSH_WAVE_STAGES_AGG 2
 #endif
 constexpr int WNS = 2;
 constexpr int WNS_AGG = ESSH_WAVE_STAGES_AGG;
