@@ -118,6 +118,8 @@ essh_status essh_mixer_prefill(const essh_dims* d,
         ScanPlan plan = plan_chunked(d->B, d->L, d->K_T, d->m, d->P, lc, d->ctrl_per_mode);
         bind_workspace(plan, workspace, d->m, d->P);
         e = launch_prefill_chunked(a, d->m, d->P, plan, stream);
+    } else if (d->io_dtype == ESSH_F32 && !d->ctrl_per_mode) {
+        e = launch_prefill_f32_chunked(a, d->m, d->P, stream);
     } else {
         e = launch_prefill_sequential(a, d->m, d->P, d->io_dtype, stream);
     }

@@ -124,6 +124,7 @@ struct ScanPlan {
 
 // Launchers (host side).  Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_sequential(const PrefillArgs& a, int m, int P, int io_dtype, hipStream_t s);
+hipError_t launch_prefill_f32_chunked(const PrefillArgs& a, int m, int P, hipStream_t s);
 bool chunked_supported(int m, int P, int Lc, int io_dtype, int per_mode);
 ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode);
 size_t chunked_workspace_bytes(int B, int L, int K_T, int m, int P, int Lc, int per_mode);

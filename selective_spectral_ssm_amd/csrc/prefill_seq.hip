@@ -4,9 +4,10 @@
 // the m complex mode states of that lane in registers while it walks the
 // positions in order.  This is the recurrence of the ESSH selective mixer
 // (Sec. 4.1 Eq. 5, readout Eq. 9) in complex form (App. B.1), evaluated
-// exactly as written, in fp32.  It serves the layouts the chunked MFMA kernel
-// does not take (fp32 io, per-mode controls); the tile kernel in
-// prefill_chunk.hip is the fast path.
+// exactly as written, in fp32.  It serves fp32 io with per-mode controls, the
+// one layout no chunked kernel takes (fp32 io with per-channel controls runs on
+// the fp32 matrix cores in prefill_f32.hip, bf16 io in prefill_chunk.hip and
+// prefill_wave.hip).
 //
 // Positions are processed in blocks of SEQ_BLK; the loads of block i+1 are
 // issued before the arithmetic of block i so that HBM latency overlaps work.

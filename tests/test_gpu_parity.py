@@ -149,11 +149,13 @@ def test_prefill_scan_forms_all_shapes(name, widx, over, K_T, Lc):
 
 # Zero-lag correction (App. C.3, Eq. 24) on every prefill path: the look-back
 # and whole-sequence MFMA kernels (per-channel bf16), the three-launch scan,
-# the sequential kernel (fp32 io) and the per-mode MFMA scan.
+# the fp32 chunked kernel, the sequential kernel (fp32 io, per-mode controls)
+# and the per-mode MFMA scan.
 ZERO_LAG = [("lookback_bf16", 1, dict(B=5, L=64 * 9 + 5, K=8), 8, 64),
             ("whole_seq_bf16", 1, dict(B=16, L=200, K=24), 24, 64),
             ("three_launch_bf16", 4, dict(L=1500), 6, 128),
-            ("sequential_f32", 0, {}, 8, 0),
+            ("f32_chunked", 0, {}, 8, 0),
+            ("per_mode_f32_sequential", 0, dict(L=90, per_mode=True), 8, 0),
             ("per_mode_bf16", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
 
 
@@ -179,6 +181,41 @@ def test_prefill_state_in_out():
     inp0 = I.make_prefill_inputs(w0)
     s0 = rng.normal(0, 3.0, size=(1, w0.K, w0.m, 2, w0.P)).astype(np.float32)
     check_prefill("state_in_f32", inp0, w0.K, 0, state_in=s0)
+
+
+# fp32 io with per-channel controls: the chunked scan on the fp32 matrix cores (16-position
+# sub-blocks, Sec. 4.3 and Eq. 6), at every (m, P) it is built for, ragged tails, an entering
+# state, the zero-lag term, tiers below K, and clock spans far past the fp32 range of a factored
+# chunk (every clock factor here is an exponential of a non-positive difference).
+F32_CHUNKED = [("f32_m4_p16_tiny", 0, {}, 8),
+               ("f32_m1_p16", 0, dict(m=1, L=77), 5),
+               ("f32_m2_p32", 0, dict(m=2, P=32, L=130, K=4), 3),
+               ("f32_m4_p64", 0, dict(P=64, L=100, K=3), 3),
+               ("f32_m8_p128", 0, dict(m=8, P=128, L=65, K=2), 2),
+               ("f32_b3_one_position", 0, dict(B=3, L=1, K=2), 2)]
+
+
+@pytest.mark.parametrize("name,widx,over,K_T", F32_CHUNKED, ids=[c[0] for c in F32_CHUNKED])
+def test_prefill_f32_chunked(name, widx, over, K_T):
+    w = I.workload(widx, **over)
+    inp = I.make_prefill_inputs(w)
+    assert inp["io"] == "f32"
+    rng = np.random.default_rng(23)
+    s0 = rng.normal(0, 2.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    check_prefill(name, inp, K_T, 0)
+    check_prefill(name + "_state_in", inp, K_T, 0, state_in=s0)
+    zl = rng.uniform(0.0, 1.0, size=(w.K, w.m)).astype(np.float32)
+    check_prefill(name + "_zero_lag", inp, K_T, 0, zl=zl)
+
+
+def test_prefill_f32_chunked_large_clock_spans():
+    w = I.workload(0, L=230, K=4)
+    inp = I.make_prefill_inputs(w)
+    d = inp["delta"]
+    d[:, 40:56] = 25.0
+    d[:, 97:101] = 12.0
+    d[:, 150:152] = 90.0          # e^{-180}: far below the fp32 range
+    check_prefill("f32_large_spans", inp, w.K, 0)
 
 
 def test_prefill_per_mode_controls():
@@ -578,7 +615,7 @@ def test_state_init_zero_fills_every_layer_and_channel():
 GATES_2SIGMA = [("lookback", 1, dict(B=5, L=64 * 9 + 5, K=8), 8, 64),
                 ("whole_seq", 1, dict(B=16, L=200, K=24), 24, 64),
                 ("three_launch", 4, dict(L=1500), 6, 128),
-                ("sequential_f32", 0, {}, 8, 0),
+                ("f32_chunked", 0, {}, 8, 0),
                 ("per_mode", 1, dict(B=2, L=90, K=3, per_mode=True), 3, 64)]
 
 
