@@ -288,6 +288,52 @@ def decode_case(K_T, n_steps=1024, reps=3, context=2048):
                 achieved_GBs_eager_events=nbytes / (kmean * 1e-6) / 1e9)
 
 
+def decode_fused_case(K_T, steps=20, warmup=3):
+    """The fused decode step with projections at the decode workload's layer shape (24 layers,
+    B=1, K=32, m=8, P=128, d = K P = 4096): random-init bf16 weights drawn on the GPU from a
+    seeded generator; events around `steps` back-to-back steps (two launches each)."""
+    import torch
+    from selective_spectral_ssm_amd import essh, inputs as I, sizes
+    w = I.workload(3)
+    NL, B, K, m, P = w.layers, w.B, w.K, w.m, w.P
+    D = K * P
+    key = ("fused",)
+    if key not in _CACHE:
+        _CACHE.clear()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed)
+
+        def randn(*shape, std=1.0):
+            return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+        t = dict(u=randn(NL, B, D), w_in=randn(NL, K, P, D, std=D ** -0.5),
+                 w_ctl=randn(NL, K, m, 3, D, std=D ** -0.5), w_out=randn(NL, D, K, P, std=(K * P) ** -0.5),
+                 beta=torch.rand(NL, K, generator=g, device="cuda") * 2 - 0.5,
+                 b_ctl=torch.randn(NL, K, m, 3, generator=g, device="cuda") - torch.tensor([0., 0., 2.], device="cuda"),
+                 rho=torch.rand(NL, K, m, generator=g, device="cuda") * (w.rho_hi - w.rho_lo) + w.rho_lo,
+                 theta=torch.rand(NL, K, m, generator=g, device="cuda") * 3.141592653589793,
+                 c=torch.randn(NL, K, m, 2, generator=g, device="cuda") * (2 * m) ** -0.5,
+                 state=torch.randn(NL, B, K, m, 2, P, generator=g, device="cuda"))
+        _CACHE[key] = t
+    t = _CACHE[key]
+    z = torch.empty(NL, B, K, P, device="cuda")
+    y = torch.empty(NL, B, D, device="cuda")
+    dims = essh.make_dims(B, 1, K, m, P, K_T, 0, False, "bf16")
+
+    def step():
+        rc = essh.essh_decode_fused_step(NL, dims, D, t["u"], t["w_in"], t["beta"], 1e-5, t["w_ctl"], t["b_ctl"],
+                                         t["rho"], t["theta"], t["c"], None, t["w_out"], t["state"], z, y)
+        assert rc == 0
+
+    _, ms_launch, ms_med = time_launches(step, steps, warmup)
+    nbytes = sizes.decode_fused_bytes(NL, B, K_T, m, P, D, "bf16")
+    us = ms_launch * 1e3
+    return dict(layers=NL, d_model=D, K_T=K_T, us_per_step=us, us_per_step_median=ms_med * 1e3,
+                alg_bytes_per_step=nbytes, achieved_GBs=nbytes / (us * 1e-6) / 1e9,
+                frac_of_hbm_peak=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                tflops=sizes.decode_fused_flops(NL, B, K_T, m, P, D) / (us * 1e-6) / 1e12)
+
+
 def _lscpu_model():
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
@@ -398,7 +444,8 @@ def main():
         for kt in I.WORKLOADS[3].tiers:
             log(f"decode: 24 layers K_T={kt}")
             out.append(decode_case(kt))
-        print(json.dumps({"decode_tiers": out}))
+        fz = [decode_fused_case(kt) for kt in (8, 16, 24, 32)]
+        print(json.dumps({"decode_tiers": out, "decode_fused": fz}))
         return
     widx, KT = args.workload, args.kt
     wname = I.WORKLOADS[widx].name
@@ -448,6 +495,11 @@ def main():
     if not args.no_decode:
         log("decode: 24 layers K_T=32")
         res["decode"] = decode_case(32)
+        fz = []
+        for kt in (8, 16, 24, 32):
+            log(f"fused decode with projections: 24 layers K_T={kt}")
+            fz.append(decode_fused_case(kt))
+        res["decode_fused"] = fz
     if not args.no_extra:
         extra = []
         for wi in (1, 2, 4):

@@ -204,6 +204,45 @@ essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
                                    const float* rho, const float* theta, const float* c, const float* zl,
                                    float* state, void* y, hipStream_t stream);
 
+/*
+ * essh_decode_fused_step -- one token through n_layers independent mixer layers, the
+ * projections included (the fused recurrent decode of Sec. 4.3 / Sec. 5.3 with App. C.2,
+ * C.3 and C.4):
+ *   v0_k = W_in_k u, then the channel-local blend of Eq. 23,
+ *          v_k = (1 - beta_k) v0_k + beta_k v0_k / sqrt(P^-1 |v0_k|^2 + eps_norm);
+ *   per (channel, mode): write gate 2 sigmoid(w.u + b), read gate 2 sigmoid(w.u + b),
+ *          clock increment softplus(w.u + b)  (App. C.2);
+ *   the mode update and readout with those per-mode controls and, when zl is given, the
+ *          zero-lag term (Eq. 5, Eq. 24): z_k;
+ *   y = K_T^-1/2 sum_{k < K_T} W_out_k z_k  (App. C.4).
+ * Channels k >= K_T are never read, computed or written.  Each weight byte is read once.
+ *
+ *   n_layers   >= 1 independent layers in one call (arrays stacked on a leading axis)
+ *   d          dims of one mixer: B, K, m, P, K_T and io_dtype (the dtype of u); L, Lc and
+ *              ctrl_per_mode are ignored (the controls are per mode, computed here)
+ *   d_model    model width: a multiple of 8, at most 8192; K_T * P at most 8192
+ *   u          [n_layers, B, d_model] io dtype: the normalized mixer input
+ *   w_in       [n_layers, K, P, d_model] bf16, 16-byte aligned: row (k, p) of W_in
+ *   beta       [n_layers, K] fp32 blend coefficients;  eps_norm > 0
+ *   w_ctl      [n_layers, K, m, 3, d_model] bf16, 16-byte aligned: rows (write gate,
+ *              read gate, clock) of each (channel, mode)
+ *   b_ctl      [n_layers, K, m, 3] fp32: their biases
+ *   rho, theta [n_layers, K, m] fp32; c [n_layers, K, m, 2] fp32; zl [n_layers, K, m] or NULL
+ *   w_out      [n_layers, d_model, K, P] bf16, 16-byte aligned: row o of W_out, its columns
+ *              grouped by channel (the first K_T P columns are read)
+ *   state      [n_layers, B, K, m, 2, P] fp32, updated in place (channels < K_T)
+ *   z          [n_layers, B, K, P] fp32 out: corrected channel outputs (channels < K_T)
+ *   y          [n_layers, B, d_model] fp32 out
+ *   stream     HIP stream to enqueue on (two launches).
+ * Accumulation is fp32.  Returns ESSH_ERR_UNSUPPORTED for d_model or K_T * P outside the
+ * bounds above, or B, n_layers or K_T above 65535.  Buffers must not overlap.
+ */
+essh_status essh_decode_fused_step(int32_t n_layers, const essh_dims* d, int32_t d_model, const void* u,
+                                   const void* w_in, const float* beta, float eps_norm, const void* w_ctl,
+                                   const float* b_ctl, const float* rho, const float* theta, const float* c,
+                                   const float* zl, const void* w_out, float* state, float* z, float* y,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

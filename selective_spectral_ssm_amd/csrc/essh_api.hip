@@ -161,4 +161,53 @@ essh_status essh_mixer_decode_step(int32_t n_layers, const essh_dims* d,
     return from_hip(launch_decode(a, d->m, d->P, d->io_dtype, stream));
 }
 
+essh_status essh_decode_fused_step(int32_t n_layers, const essh_dims* d, int32_t d_model, const void* u,
+                                   const void* w_in, const float* beta, float eps_norm, const void* w_ctl,
+                                   const float* b_ctl, const float* rho, const float* theta, const float* c,
+                                   const float* zl, const void* w_out, float* state, float* z, float* y,
+                                   hipStream_t stream) {
+    essh_status st = check_dims(d, false);
+    if (st != ESSH_OK) return st;
+    if (n_layers < 1 || !(eps_norm > 0.f) || eps_norm > 3.0e38f) return ESSH_ERR_INVALID_ARG;
+    const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
+    if (!u || !w_in || !beta || !w_ctl || !b_ctl || !rho || !theta || !c || !w_out || !state || !z || !y)
+        return ESSH_ERR_INVALID_ARG;
+    if (!aligned(u, io) || !aligned(w_in, 16) || !aligned(w_ctl, 16) || !aligned(w_out, 16) || !aligned(beta, 4) ||
+        !aligned(b_ctl, 4) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4) || (zl && !aligned(zl, 4)) ||
+        !aligned(state, 4) || !aligned(z, 4) || !aligned(y, 4))
+        return ESSH_ERR_INVALID_ARG;
+    // u staged in LDS, 16-byte weight loads; the retained channel outputs staged in LDS
+    if (d_model < 8 || d_model % 8 != 0 || d_model > 8192 || (long long)d->K_T * d->P > 8192)
+        return ESSH_ERR_UNSUPPORTED;
+    if (d->B > 65535 || n_layers > 65535 || d->K_T > 65535) return ESSH_ERR_UNSUPPORTED;   // grid extents
+    if ((long long)n_layers * d->B * d->K * d->P > (1LL << 30) ||
+        (long long)n_layers * d->K * d->P * d_model > (1LL << 40))
+        return ESSH_ERR_UNSUPPORTED;
+    if (d->B == 0) return ESSH_OK;
+
+    FusedDecodeArgs a{};
+    a.n_layers = n_layers;
+    a.B = d->B;
+    a.K = d->K;
+    a.K_T = d->K_T;
+    a.m = d->m;
+    a.P = d->P;
+    a.d_model = d_model;
+    a.eps_norm = eps_norm;
+    a.u = u;
+    a.w_in = static_cast<const uint16_t*>(w_in);
+    a.beta = beta;
+    a.w_ctl = static_cast<const uint16_t*>(w_ctl);
+    a.b_ctl = b_ctl;
+    a.rho = rho;
+    a.theta = theta;
+    a.c = c;
+    a.zl = zl;
+    a.w_out = static_cast<const uint16_t*>(w_out);
+    a.state = state;
+    a.z = z;
+    a.y = y;
+    return from_hip(launch_decode_fused(a, d->io_dtype, stream));
+}
+
 }  // extern "C"

@@ -72,6 +72,24 @@ struct DecodeArgs {
     void* y;
 };
 
+struct FusedDecodeArgs {
+    int n_layers, B, K, K_T, m, P, d_model;
+    float eps_norm;
+    const void* u;            // [n_layers, B, d_model] io dtype
+    const uint16_t* w_in;     // [n_layers, K, P, d_model] bf16
+    const float* beta;        // [n_layers, K]
+    const uint16_t* w_ctl;    // [n_layers, K, m, 3, d_model] bf16
+    const float* b_ctl;       // [n_layers, K, m, 3]
+    const float* rho;
+    const float* theta;
+    const float* c;
+    const float* zl;          // or null
+    const uint16_t* w_out;    // [n_layers, d_model, K, P] bf16
+    float* state;             // [n_layers, B, K, m, 2, P]
+    float* z;                 // [n_layers, B, K, P]
+    float* y;                 // [n_layers, B, d_model]
+};
+
 // Work split of the chunked prefill.  nseq = B * K_T sequences of nchunks
 // chunks; each sequence is cut into nseg segments of seg_chunks chunks, one
 // workgroup per (sequence, segment).  With nseg > 1 the workspace holds the
@@ -138,6 +156,7 @@ hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s);
 // look-back flags); 0 when the plan keeps no look-back records.
 size_t prefill_clear_bytes(const essh_dims* d);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int B, int K, int K_T, int m, int P, hipStream_t s);
 

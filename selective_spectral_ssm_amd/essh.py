@@ -26,7 +26,7 @@ ESSH_F32, ESSH_BF16 = 0, 1
 # Every symbol the C header declares (checked by the tests against include/essh.h).
 EXPORTED = ("essh_abi_version", "essh_status_string", "essh_state_init",
             "essh_prefill_workspace_bytes", "essh_mixer_prefill", "essh_mixer_prefill_noalloc",
-            "essh_mixer_decode_step")
+            "essh_mixer_decode_step", "essh_decode_fused_step")
 
 
 class EsshLibraryMissing(RuntimeError):
@@ -84,6 +84,9 @@ def lib():
         L.essh_mixer_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12 + [SZ, P]
         L.essh_mixer_prefill_noalloc.restype = ctypes.c_int
         L.essh_mixer_prefill_noalloc.argtypes = [ctypes.POINTER(Dims)] + [P] * 13
+        L.essh_decode_fused_step.restype = ctypes.c_int
+        L.essh_decode_fused_step.argtypes = ([I32, ctypes.POINTER(Dims), I32] + [P] * 3 + [ctypes.c_float]
+                                             + [P] * 11)
         L.essh_mixer_decode_step.restype = ctypes.c_int
         L.essh_mixer_decode_step.argtypes = [I32, ctypes.POINTER(Dims)] + [P] * 10 + [P]
         _lib = L
@@ -153,6 +156,15 @@ def essh_mixer_prefill_noalloc(dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl
     return lib().essh_mixer_prefill_noalloc(ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w), _ptr(g_r),
                                             _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl), _ptr(state_in),
                                             _ptr(state_out), _ptr(y), _ptr(scan_error), _stream(stream))
+
+
+def essh_decode_fused_step(n_layers: int, dims: Dims, d_model: int, u, w_in, beta, eps_norm: float, w_ctl, b_ctl,
+                           rho, theta, c, zl, w_out, state, z, y, stream=None) -> int:
+    """Direct call of the fused decode step with projections; returns the status code."""
+    return lib().essh_decode_fused_step(int(n_layers), ctypes.byref(dims), int(d_model), _ptr(u), _ptr(w_in),
+                                        _ptr(beta), float(eps_norm), _ptr(w_ctl), _ptr(b_ctl), _ptr(rho),
+                                        _ptr(theta), _ptr(c), _ptr(zl), _ptr(w_out), _ptr(state), _ptr(z), _ptr(y),
+                                        _stream(stream))
 
 
 def essh_mixer_decode_step(n_layers: int, dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state, y,

@@ -184,6 +184,34 @@ def make_decode_inputs(w: Workload, n_steps: Optional[int] = None, context: Opti
                 step_v=sv, step_delta=sd, step_g_w=sgw, step_g_r=sgr, io=w.io)
 
 
+def make_fused_decode_inputs(NL: int, B: int, K: int, m: int, P: int, d_model: int, io: str = "bf16",
+                             seed: int = SEED_BASE + 3, rho_lo: float = 0.95, rho_hi: float = 0.9999) -> dict:
+    """Synthetic inputs of the fused decode step with projections (random-init weights of the
+    layout the library takes, drawn as the decode workload draws its mode tables).
+
+    u [NL,B,d] (io); w_in [NL,K,P,d], w_ctl [NL,K,m,3,d], w_out [NL,d,K,P] as bf16 bits, entries
+    N(0, 1/fan_in); beta [NL,K] ~ U(-0.5, 1.5); b_ctl [NL,K,m,3]: gate biases N(0,1), clock
+    biases N(-2, 1); rho, theta, c as the decode workload; zl [NL,K,m] ~ U(0,1);
+    state [NL,B,K,m,2,P] ~ N(0,1) (fp32)."""
+    rng = np.random.default_rng(seed)
+    rho = np.empty((NL, K, m), np.float32)
+    theta = np.empty_like(rho)
+    c = np.empty((NL, K, m, 2), np.float32)
+    for l in range(NL):
+        rho[l], theta[l], c[l] = draw_params(rng, K, m, rho_lo, rho_hi)
+    u = _io_array(rng.normal(0.0, 1.0, size=(NL, B, d_model)), io)
+    w_in = f32_to_bf16_bits(rng.normal(0.0, 1.0 / np.sqrt(d_model), size=(NL, K, P, d_model)).astype(np.float32))
+    w_ctl = f32_to_bf16_bits(rng.normal(0.0, 1.0 / np.sqrt(d_model), size=(NL, K, m, 3, d_model)).astype(np.float32))
+    w_out = f32_to_bf16_bits(rng.normal(0.0, 1.0 / np.sqrt(K * P), size=(NL, d_model, K, P)).astype(np.float32))
+    beta = rng.uniform(-0.5, 1.5, size=(NL, K)).astype(np.float32)
+    b_ctl = rng.normal(0.0, 1.0, size=(NL, K, m, 3))
+    b_ctl[..., 2] -= 2.0
+    zl = rng.uniform(0.0, 1.0, size=(NL, K, m)).astype(np.float32)
+    state = rng.normal(0.0, 1.0, size=(NL, B, K, m, 2, P)).astype(np.float32)
+    return dict(u=u, w_in=w_in, w_ctl=w_ctl, w_out=w_out, beta=beta, b_ctl=b_ctl.astype(np.float32), rho=rho,
+                theta=theta, c=c, zl=zl, state=state, io=io, d_model=d_model)
+
+
 def as_f64(x: np.ndarray, io: str) -> np.ndarray:
     """Exact float64 view of an io array (bf16 bits or float32)."""
     if x.dtype == np.uint16:

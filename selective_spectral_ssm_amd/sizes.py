@@ -51,5 +51,21 @@ def decode_bytes(n_layers: int, B: int, K_T: int, m: int, P: int, io: str) -> in
     return n_layers * B * K_T * per
 
 
+def decode_fused_bytes(n_layers: int, B: int, K_T: int, m: int, P: int, d_model: int, io: str,
+                       zero_lag: bool = False) -> int:
+    """Fused decode step with projections: the retained rows of W_in (K_T P x d) and of the gate
+    and clock projections (3 K_T m x d) and the first K_T P columns of W_out, all bf16, their
+    biases and blend coefficients, the modal tables; per batch row u, the state read and
+    written, z and y (fp32)."""
+    s = IO_BYTES[io]
+    weights = 2 * d_model * (2 * K_T * P + 3 * K_T * m) + 4 * (3 * K_T * m + K_T) + K_T * m * (16 + (4 if zero_lag else 0))
+    per_row = d_model * s + 2 * 8 * K_T * m * P + 4 * K_T * P + 4 * d_model
+    return n_layers * (weights + B * per_row)
+
+
+def decode_fused_flops(n_layers: int, B: int, K_T: int, m: int, P: int, d_model: int) -> int:
+    return n_layers * B * (2 * d_model * (2 * K_T * P + 3 * K_T * m) + K_T * (10 * m * P + 2 * P))
+
+
 def decode_flops(n_layers: int, B: int, K_T: int, m: int, P: int) -> int:
     return n_layers * B * K_T * (10 * m * P + 2 * P)

@@ -41,6 +41,28 @@ def test_status_strings(lib):
         assert essh.status_string(code).startswith("ESSH_")
 
 
+def test_decode_fused_validation(lib):
+    """Host-side checks of the fused decode step: nothing is launched on these paths."""
+    f = ctypes.c_void_p(FAKE)
+    d = essh.make_dims(1, 1, 32, 8, 128, 32, 0)
+
+    def call(n_layers=1, dims=d, d_model=4096, eps=1e-5, zl=None, u=f):
+        return lib.essh_decode_fused_step(n_layers, ctypes.byref(dims), d_model, u, f, f, eps, f, f, f, f, f, zl, f,
+                                          f, f, f, None)
+    assert call(d_model=4100) == essh.ESSH_ERR_UNSUPPORTED          # not a multiple of 8
+    assert call(d_model=8200) == essh.ESSH_ERR_UNSUPPORTED          # wider than the staged input
+    assert call(eps=0.0) == essh.ESSH_ERR_INVALID_ARG
+    assert call(eps=-1.0) == essh.ESSH_ERR_INVALID_ARG
+    assert call(n_layers=0) == essh.ESSH_ERR_INVALID_ARG
+    assert call(u=None) == essh.ESSH_ERR_INVALID_ARG
+    wide = essh.make_dims(1, 1, 128, 8, 128, 128, 0)                # K_T P = 16384 > 8192
+    assert call(dims=wide) == essh.ESSH_ERR_UNSUPPORTED
+    bad_kt = essh.make_dims(1, 1, 32, 8, 128, 33, 0)
+    assert call(dims=bad_kt) == essh.ESSH_ERR_INVALID_ARG
+    assert lib.essh_decode_fused_step(1, ctypes.byref(d), 4096, f, ctypes.c_void_p(FAKE + 8), f, 1e-5, f, f, f, f,
+                                      f, None, f, f, f, f, None) == essh.ESSH_ERR_INVALID_ARG   # weights misaligned
+
+
 def test_noalloc_scratch_limit(lib):
     """The allocation-free prefill refuses, before launching anything, dims whose look-back
     records exceed its static scratch, and validates dims like the workspace entry point."""
