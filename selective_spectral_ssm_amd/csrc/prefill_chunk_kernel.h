@@ -296,16 +296,19 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(uint2 a, uint2 b) {
 enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2, MODE_STREAM_PM = 3, MODE_AGG_PM = 4 };
 
 // Workgroups per CU that the register budget is held to.  Look-back launches
-// keep a workgroup's chunks resident in LDS, four workgroups per CU, and match
-// that.  Streaming and per-mode launches with up to four modes fit three
-// workgroups in 168 VGPRs without spilling.  Measured on MI355X against the
+// keep a workgroup's chunks resident in LDS (four workgroups per CU would fit);
+// with the carry readout's coefficients held in hi and lo halves their operands
+// need three workgroups' budget (168 VGPRs): four spilled 80-130 bytes per lane
+// and ran 370M-class tiers 15-25% slower, three runs them level with or faster
+// than the former four without the lo halves.  Streaming and per-mode launches
+// with up to four modes fit three workgroups in 168 VGPRs without spilling.  Measured on MI355X against the
 // unbounded two: the per-mode three-launch scan 16-17% faster (370M-class,
 // K_T = 6..24), the 128K-token three-launch scan 2-10% faster (K_T = 24..6).
 // Four spilled and was slower.
 template <class C, int MODE>
 constexpr int min_workgroups_per_cu() {
     if (C::NW != 4 || C::M > 4) return 1;
-    if (MODE == MODE_LOOKBACK) return 4;
+    if (MODE == MODE_LOOKBACK) return 3;
     if (MODE == MODE_STREAM || MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM) return 3;
     return 1;
 }
@@ -597,7 +600,10 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // Output product of target sub-block a of a block (B operands; lane (g, col)
     // is target position t = 16a + col of the block):
     //   yD[a]: slots 0..3: psi(t-s) [s <= t] for s = 16a+4g+e (same for every a);
-    //          slots 4..7: {Re, -Im}(c_j lambda_j^{t+1}) for state rows 4g..4g+3.
+    //          slots 4..7: {Re, -Im}(c_j lambda_j^{t+1}) for state rows 4g..4g+3, bf16 hi.
+    //   yDx[a]: slots 0..3: the bf16 lo halves of those coefficients, slots 4..7: their hi
+    //          halves; against [state hi ; state lo] it adds both cross terms of the carry
+    //          readout, whose mode terms may cancel (fitted tables carry |c| up to ~30).
     //   yB12:  slots 0..3: psi(16+col-4g-e) (source sub-block a-1),
     //          slots 4..7: psi(32+col-4g-e) (source sub-block a-2).
     //   yB3:   slots 0..3: psi(48+col-4g-e) (source sub-block a-3), slots 4..7: 0.
@@ -610,8 +616,24 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // The output operands (yD, yB12, yB3) and the state operands (lpA, lB, l16)
     // are built separately: the look-back launch needs the state operands in
     // its aggregate sweep and the output operands in its output sweep only.
-    bf16x8_t yD[NB], yB12, yB3, lpA[NB];
+    bf16x8_t yD[NB], yDx[NB], yB12, yB3, lpA[NB];
     float lB[4], l16[4];
+    auto make_ydx = [&](int aa) __attribute__((always_inline)) -> bf16x8_t {
+        u16x8_t hx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * g + i, j = row >> 1;
+            float val = 0.f;
+            if (j < M) {
+                const float2 cp = sm.cpw[col + 1][j < M ? j : 0], pd = sm.pw[17 + aa][j < M ? j : 0];
+                val = (row & 1) ? -(cp.x * pd.y + cp.y * pd.x) : (cp.x * pd.x - cp.y * pd.y);
+            }
+            const uint16_t hb = f32_to_bf16(val);
+            hx[4 + i] = hb;
+            hx[i] = f32_to_bf16(val - bf16_to_f32(hb));
+        }
+        return to_bf16x8(hx);
+    };
     auto make_out_constants = [&]() __attribute__((always_inline)) {
         u16x8_t h;
 #pragma unroll
@@ -632,6 +654,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 h[4 + i] = f32_to_bf16(val);
             }
             yD[aa] = to_bf16x8(h);
+            yDx[aa] = make_ydx(aa);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1014,7 +1037,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     const uint2 hh = hi4(st[nt]);
                     f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         bf16x8_of(bv[nt], hh), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), yD[0], acc, 0,
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), yDx[0], acc, 0,
                                                                   0, 0);
                     stage_y(T, nt, acc, sc);
                 }
@@ -1068,14 +1091,17 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             av[i] = spm.fa[jj][t] * ((row & 1) ? -cp.y : cp.x);
                         }
                     }
-                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
-                                                  make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+                    // carry coefficients in bf16 hi and lo halves (mode terms may cancel)
+                    const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
+                    const uint2 ah4 = hi4(af);
+                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                    const bf16x8_t bxx = bf16x8_of(lo4(af, ah4), ah4);
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) {
                         const uint2 hh = hi4(st[nt]);
                         f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0,
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0,
                                                                       0, 0);
                         stage_y(T, nt, acc, 1.f);
                     }
@@ -1152,14 +1178,17 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             av[i] = ea * ((row & 1) ? -cp.y : cp.x);
                         }
                     }
-                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
-                                                  make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+                    // carry coefficients in bf16 hi and lo halves (mode terms may cancel)
+                    const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
+                    const uint2 ah4 = hi4(af);
+                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                    const bf16x8_t bxx = bf16x8_of(lo4(af, ah4), ah4);
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) {
                         const uint2 hh = hi4(st[nt]);
                         f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0,
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0,
                                                                       0, 0);
                         stage_y(T, nt, acc, 1.f);
                     }
@@ -1238,15 +1267,18 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     }
                     av[i] = val;
                 }
-                const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
-                                              make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+                // carry coefficients in bf16 hi and lo halves (mode terms may cancel)
+                const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
+                const uint2 ah4 = hi4(af);
+                const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                const bf16x8_t bxx = bf16x8_of(lo4(af, ah4), ah4);
                 const float sc = bf16_to_f32((uint16_t)sgp->gr[t]);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const uint2 hh = hi4(st[nt]);
                     f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, lo4(st[nt], hh)), bx, acc, 0, 0,
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0, 0,
                                                                   0);
                     stage_y(T, nt, acc, sc);
                 }
@@ -1342,7 +1374,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 for (int nt = 0; nt < NTW; ++nt) {
                     f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
                                                                          f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, hl[nt]), yD[aa], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh[nt], hl[nt]), yDx[aa], acc, 0, 0, 0);
                     if (aa >= 1)
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2),
@@ -1399,7 +1431,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             for (int nt = 0; nt < NTW; ++nt) {
                 f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(bvh[aa][nt], hh[nt]), yD[aa],
                                                                      f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(zero2, hl[nt]), yD[aa], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh[nt], hl[nt]), yDx[aa], acc, 0, 0, 0);
                 if (aa >= 1)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         bf16x8_of(bvh[aa >= 1 ? aa - 1 : 0][nt], aa >= 2 ? bvh[aa >= 2 ? aa - 2 : 0][nt] : z2), yB12,

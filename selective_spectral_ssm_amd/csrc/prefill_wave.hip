@@ -22,9 +22,10 @@
 // value column, so the operands that carry them are formed once per block and shared by the
 // four tiles, and v enters every v_mfma_f32_16x16x32_bf16 exactly as read from LDS:
 //   output, target sub-block a (B operands, lane (g, col) = target position t = 16a + col):
-//     [ g_r a(t) b(s) psi(t-s) for s in sub-block a ; g_r a(t) Hs {Re,-Im}(c lambda^{t+1}) ]
-//     against A = [ v(s) ; state hi ] and [ 0 ; state lo ]; then the pieces of the three
-//     preceding sub-blocks against A = [ v ; v ].
+//     [ g_r a(t) b(s) psi(t-s) for s in sub-block a ; C hi ] against A = [ v(s) ; state hi ],
+//     and [ C lo ; C hi ] against A = [ state hi ; state lo ], with C = g_r a(t) Hs
+//     {Re,-Im}(c lambda^{t+1}) split into bf16 halves (the modes' readout terms may cancel);
+//     then the pieces of the three preceding sub-blocks against A = [ v ; v ].
 //   state, source sub-block a (A operand, lane (g, col) = state row (mode, re/im)):
 //     {Re, Im}(lambda^{63-s}) b(s) split into bf16 hi and lo halves, against B = [ v ; v ],
 //     so the state product is exact up to the lambda-power and b(s) rounding to ~16 bits.
@@ -422,14 +423,19 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
                                           lw[aa][3] * bqv[aa][3]};
                 const uint2 wh = hi4(w);
                 const bf16x8_t W = bf16x8_of(wh, lo4(w, wh));
-                bf16x8_t Bd, B12, B3;
+                bf16x8_t Bd, Bx, B12, B3;
                 if constexpr (!AGG) {
                     const float at = __shfl(agl, 16 * aa + col);
                     const float ah = at * Hs;
+                    // the carry readout's coefficients in bf16 hi and lo halves: the modes'
+                    // terms may cancel (fitted tables carry |c| up to ~30 for outputs ~0.1)
+                    const f32x4_t cf = f32x4_t{ah * c0[aa][0], ah * c0[aa][1], ah * c0[aa][2], ah * c0[aa][3]};
+                    const uint2 ch = hi4(cf);
                     Bd = bf16x8_of(
                         make_uint2(pk_bf16(at * bqv[aa][0] * psv[0][0], at * bqv[aa][1] * psv[0][1]),
                                    pk_bf16(at * bqv[aa][2] * psv[0][2], at * bqv[aa][3] * psv[0][3])),
-                        make_uint2(pk_bf16(ah * c0[aa][0], ah * c0[aa][1]), pk_bf16(ah * c0[aa][2], ah * c0[aa][3])));
+                        ch);
+                    Bx = bf16x8_of(lo4(cf, ch), ch);
                     if (aa >= 1) {
                         const int a1 = aa >= 1 ? aa - 1 : 0, a2 = aa >= 2 ? aa - 2 : 0;
                         const float s2 = aa >= 2 ? at : 0.f;
@@ -450,7 +456,8 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
                     mv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W, bf16x8_of(v0, v0), mv[nt], 0, 0, 0);
                     if constexpr (!AGG) {
                         f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(v0, hh[nt]), Bd, zf, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(z2, hl[nt]), Bd, acc, 0, 0, 0);
+                        // state hi x coefficient lo + state lo x coefficient hi
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh[nt], hl[nt]), Bx, acc, 0, 0, 0);
                         if (aa >= 1) {
                             const uint2 v1 = vfrag(sv, aa >= 1 ? aa - 1 : 0, nt);
                             const uint2 v2 = aa >= 2 ? vfrag(sv, aa >= 2 ? aa - 2 : 0, nt) : z2;
@@ -509,13 +516,15 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
                         const float2 cp = tb.cpw[col + 1][j < M ? j : 0];
                         av[i] = j < M ? ea * ((row & 1) ? -cp.y : cp.x) : 0.f;
                     }
-                    const bf16x8_t Bo = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])),
-                                                  make_uint2(pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])));
+                    const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
+                    const uint2 ah4 = hi4(af);
+                    const bf16x8_t Bo = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                    const bf16x8_t Box = bf16x8_of(lo4(af, ah4), ah4);
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
                         const uint2 hh = hi4(st[nt]);
                         f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(vf[nt], hh), Bo, zf, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(z2, lo4(st[nt], hh)), Bo, acc, 0, 0,
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), Box, acc, 0, 0,
                                                                       0);
                         stage_y(sv, T, nt, acc);
                     }

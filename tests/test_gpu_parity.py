@@ -218,6 +218,20 @@ def test_prefill_f32_chunked_large_clock_spans():
     check_prefill("f32_large_spans", inp, w.K, 0)
 
 
+def test_prefill_fitted_mode_tables():
+    """Mode tables from the Hankel filter bank's matrix-pencil fit (App. C.1.1: poles up to
+    |lambda| = 0.9998, both rotation senses) on the MFMA paths: the one-wave three-launch scan,
+    the look-back and whole sequences."""
+    from selective_spectral_ssm_amd import modefit
+    tabs = modefit.fit_mode_tables(8, 8, L=2048)
+    for name, B, L, K_T in (("fitted_three_launch", 1, 700, 8), ("fitted_lookback", 5, 64 * 9 + 5, 8),
+                            ("fitted_whole_seq", 48, 150, 8)):
+        w = I.workload(1, B=B, L=L, K=8, m=8)
+        inp = I.make_prefill_inputs(w)
+        inp["rho"], inp["theta"], inp["c"] = tabs["rho"], tabs["theta"], tabs["c"]
+        check_prefill(name, inp, K_T, 64)
+
+
 def test_prefill_per_mode_controls():
     for widx, over in ((0, dict(L=90)), (1, dict(B=1, L=70, K=3))):
         w = I.workload(widx, **over)
