@@ -243,6 +243,50 @@ essh_status essh_decode_fused_step(int32_t n_layers, const essh_dims* d, int32_t
                                    const float* zl, const void* w_out, float* state, float* z, float* y,
                                    hipStream_t stream);
 
+/*
+ * essh_prefill_backward_workspace_bytes -- device workspace, in bytes, that
+ * essh_mixer_prefill_backward needs for dims d (0 if d is invalid).
+ */
+size_t essh_prefill_backward_workspace_bytes(const essh_dims* d);
+
+/*
+ * essh_mixer_prefill_backward -- gradients of the prefill (training's backward pass).
+ *
+ * Differentiates the computation of essh_mixer_prefill (Sec. 4.1 Eq. 5, Eq. 9, and App. C.3
+ * Eq. 24 when zl is given) for a loss L with dL/dy = dy and dL/dstate_out = dstate_out, by
+ * the chunked scan of Sec. 4.3 run backwards: the adjoint of each mode state runs from the
+ * last position to the first with the conjugate poles, and only the 2 m P mode-state entries
+ * of a channel (and their adjoints) cross sub-block and segment boundaries.
+ *
+ *   d          dims as for the prefill; ctrl_per_mode must be 0 (per-channel controls);
+ *              Lc is ignored (sub-blocks of 16 positions).  B * K_T at most 65535.
+ *   v .. zl, state_in   the forward inputs, exactly as passed to essh_mixer_prefill
+ *   dy         [B, L, K, P] io dtype, 16-byte aligned: dL/dy
+ *   dstate_out [B, K, m, 2, P] fp32 or NULL (the final state carries no gradient)
+ *   dv         [B, L, K, P] io dtype, 16-byte aligned, out: dL/dv
+ *   ddelta     [B, L, K] fp32 out: dL/ddelta
+ *   dg_w, dg_r [B, L, K] fp32 out (also for bf16 io): dL/dg_w, dL/dg_r
+ *   drho, dtheta [K, m] fp32 out;  dc [K, m, 2] fp32 out (d/dRe c, d/dIm c)
+ *   dzl        [K, m] fp32 out or NULL: dL/dzl (evaluated at zl, or at zero when zl is NULL)
+ *   dstate_in  [B, K, m, 2, P] fp32 out or NULL: dL/dstate_in
+ *   workspace  device memory of at least essh_prefill_backward_workspace_bytes(d) bytes,
+ *              256-byte aligned, owned by the caller; no contents need to be preserved
+ *   stream     HIP stream to enqueue on (four or five launches).
+ * Every output of channels k < K_T is overwritten (the mode-table gradients are sums over
+ * the batch and all positions, not accumulated into the caller's values); entries of channels
+ * k >= K_T are never read or written.  Arithmetic is fp32 throughout (fp32 matrix cores).
+ * Returns ESSH_ERR_UNSUPPORTED for ctrl_per_mode = 1 or B * K_T above 65535,
+ * ESSH_ERR_WORKSPACE when the workspace is missing, misaligned or too small.  Output buffers
+ * must not overlap inputs or each other.
+ */
+essh_status essh_mixer_prefill_backward(const essh_dims* d,
+                                        const void* v, const float* delta, const void* g_w, const void* g_r,
+                                        const float* rho, const float* theta, const float* c, const float* zl,
+                                        const float* state_in, const void* dy, const float* dstate_out,
+                                        void* dv, float* ddelta, float* dg_w, float* dg_r,
+                                        float* drho, float* dtheta, float* dc, float* dzl, float* dstate_in,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libessh.so")
 SOURCES = ["essh_api.hip", "prefill_seq.hip", "prefill_chunk.hip", "prefill_chunk_pm.hip", "prefill_wave.hip",
-           "decode.hip", "noalloc.hip", "prefill_f32.hip", "decode_fused.hip"]
+           "decode.hip", "noalloc.hip", "prefill_f32.hip", "decode_fused.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

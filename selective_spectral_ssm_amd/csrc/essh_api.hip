@@ -210,4 +210,77 @@ essh_status essh_decode_fused_step(int32_t n_layers, const essh_dims* d, int32_t
     return from_hip(launch_decode_fused(a, d->io_dtype, stream));
 }
 
+size_t essh_prefill_backward_workspace_bytes(const essh_dims* d) {
+    if (check_dims(d, true) != ESSH_OK || d->ctrl_per_mode) return 0;
+    return backward_workspace_bytes(d->B, d->L, d->K, d->K_T, d->m, d->P);
+}
+
+essh_status essh_mixer_prefill_backward(const essh_dims* d,
+                                        const void* v, const float* delta, const void* g_w, const void* g_r,
+                                        const float* rho, const float* theta, const float* c, const float* zl,
+                                        const float* state_in, const void* dy, const float* dstate_out,
+                                        void* dv, float* ddelta, float* dg_w, float* dg_r,
+                                        float* drho, float* dtheta, float* dc, float* dzl, float* dstate_in,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    essh_status st = check_dims(d, true);
+    if (st != ESSH_OK) return st;
+    if (d->ctrl_per_mode) return ESSH_ERR_UNSUPPORTED;
+    if ((long long)d->B * d->K_T > 65535) return ESSH_ERR_UNSUPPORTED;   // grid z extent
+    const size_t io = d->io_dtype == ESSH_BF16 ? 2 : 4;
+    if (!v || !delta || !g_w || !g_r || !rho || !theta || !c || !dy || !dv || !ddelta || !dg_w || !dg_r || !drho ||
+        !dtheta || !dc)
+        return ESSH_ERR_INVALID_ARG;
+    if (!aligned(v, 16) || !aligned(dy, 16) || !aligned(dv, 16) || !aligned(delta, 4) || !aligned(g_w, io) ||
+        !aligned(g_r, io) || !aligned(rho, 4) || !aligned(theta, 4) || !aligned(c, 4) || (zl && !aligned(zl, 4)) ||
+        (state_in && !aligned(state_in, 4)) || (dstate_out && !aligned(dstate_out, 4)) || !aligned(ddelta, 4) ||
+        !aligned(dg_w, 4) || !aligned(dg_r, 4) || !aligned(drho, 4) || !aligned(dtheta, 4) || !aligned(dc, 4) ||
+        (dzl && !aligned(dzl, 4)) || (dstate_in && !aligned(dstate_in, 4)))
+        return ESSH_ERR_INVALID_ARG;
+    if ((d->P * io) % 16 != 0) return ESSH_ERR_UNSUPPORTED;
+    const size_t need = backward_workspace_bytes(d->B, d->L, d->K, d->K_T, d->m, d->P);
+    if (d->B > 0 && d->L > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return ESSH_ERR_WORKSPACE;
+
+    if (d->B == 0 || d->L == 0) {
+        // no positions: the mode tables get zero gradient and the adjoint passes through
+        const size_t km = (size_t)d->K_T * d->m;
+        hipError_t e = launch_fill_zero(drho, km, stream);
+        if (e == hipSuccess) e = launch_fill_zero(dtheta, km, stream);
+        if (e == hipSuccess) e = launch_fill_zero(dc, 2 * km, stream);
+        if (e == hipSuccess && dzl) e = launch_fill_zero(dzl, km, stream);
+        if (e == hipSuccess && dstate_in)
+            e = launch_copy_state(dstate_out, dstate_in, d->B, d->K, d->K_T, d->m, d->P, stream);
+        return from_hip(e);
+    }
+
+    BackwardArgs a{};
+    a.B = d->B;
+    a.L = d->L;
+    a.K = d->K;
+    a.K_T = d->K_T;
+    a.v = v;
+    a.delta = delta;
+    a.g_w = g_w;
+    a.g_r = g_r;
+    a.rho = rho;
+    a.theta = theta;
+    a.c = c;
+    a.zl = zl;
+    a.state_in = state_in;
+    a.dy = dy;
+    a.dstate_out = dstate_out;
+    a.dv = dv;
+    a.ddelta = ddelta;
+    a.dg_w = dg_w;
+    a.dg_r = dg_r;
+    a.drho = drho;
+    a.dtheta = dtheta;
+    a.dc = dc;
+    a.dzl = dzl;
+    a.dstate_in = dstate_in;
+    BwdPlan plan = plan_backward(d->B, d->L, d->K, d->K_T, d->m, d->P);
+    bind_backward_workspace(plan, workspace, d->m);
+    return from_hip(launch_prefill_backward(a, d->m, plan, d->io_dtype, stream));
+}
+
 }  // extern "C"

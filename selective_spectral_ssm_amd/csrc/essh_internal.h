@@ -90,6 +90,53 @@ struct FusedDecodeArgs {
     float* y;                 // [n_layers, B, d_model]
 };
 
+struct BackwardArgs {
+    int B, L, K, K_T;
+    const void* v;            // forward inputs, as for the prefill
+    const float* delta;
+    const void* g_w;
+    const void* g_r;
+    const float* rho;
+    const float* theta;
+    const float* c;
+    const float* zl;          // or null
+    const float* state_in;    // or null (zero entering state)
+    const void* dy;           // [B, L, K, P] io dtype
+    const float* dstate_out;  // [B, K, m, 2, P] or null
+    void* dv;                 // [B, L, K, P] io dtype
+    float* ddelta;            // [B, L, K]
+    float* dg_w;              // [B, L, K] fp32
+    float* dg_r;              // [B, L, K] fp32
+    float* drho;              // [K, m]
+    float* dtheta;            // [K, m]
+    float* dc;                // [K, m, 2]
+    float* dzl;               // [K, m] or null
+    float* dstate_in;         // [B, K, m, 2, P] or null
+};
+
+// Work split of the backward pass: nseq = B K_T sequences, each cut into nseg segments of Ls
+// positions (nsb sub-blocks of 16), each segment handled by nslice waves of <= 64 value columns.
+// Workspace (fp32):
+//   ck   [nseq][nseg][nsb][2m][P]  local state (from a zero entering state) after each sub-block
+//   sa   [nseq][nseg][2m][P]       local adjoint aggregate, then the arriving adjoint
+//   hin  [nseq][nseg][2m][P]       entering state of each segment
+//   ltr  [nseq][nseg][nsb][m]      sub-block transfers lambda_j^n e^{-q(n-1)} (complex)
+//   lam  [nseq][nseg][m]           segment transfers (complex)
+//   pp   [nseq][nseg][nslice][4m+1] mode-table partials (Omega_j, Gamma_j, trace)
+//   part [nslice][B L K][3]        per-slice ddelta, dg_w, dg_r (nslice > 1 only)
+constexpr int MAX_BWD_SUBBLOCKS = 64;
+struct BwdPlan {
+    int P, nslice, nseq, nseg, Ls, nsb;
+    size_t nctl;              // B L K
+    float* ck;
+    float* sa;
+    float* hin;
+    float2* ltr;
+    float2* lam;
+    float* pp;
+    float* part;
+};
+
 // Work split of the chunked prefill.  nseq = B * K_T sequences of nchunks
 // chunks; each sequence is cut into nseg segments of seg_chunks chunks, one
 // workgroup per (sequence, segment).  With nseg > 1 the workspace holds the
@@ -157,6 +204,10 @@ hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s);
 size_t prefill_clear_bytes(const essh_dims* d);
 hipError_t launch_decode(const DecodeArgs& a, int m, int P, int io_dtype, hipStream_t s);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, int io_dtype, hipStream_t s);
+BwdPlan plan_backward(int B, int L, int K, int K_T, int m, int P);
+size_t backward_workspace_bytes(int B, int L, int K, int K_T, int m, int P);
+void bind_backward_workspace(BwdPlan& plan, void* workspace, int m);
+hipError_t launch_prefill_backward(const BackwardArgs& a, int m, const BwdPlan& plan, int io_dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int B, int K, int K_T, int m, int P, hipStream_t s);
 

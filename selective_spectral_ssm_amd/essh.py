@@ -26,7 +26,8 @@ ESSH_F32, ESSH_BF16 = 0, 1
 # Every symbol the C header declares (checked by the tests against include/essh.h).
 EXPORTED = ("essh_abi_version", "essh_status_string", "essh_state_init",
             "essh_prefill_workspace_bytes", "essh_mixer_prefill", "essh_mixer_prefill_noalloc",
-            "essh_mixer_decode_step", "essh_decode_fused_step")
+            "essh_mixer_decode_step", "essh_decode_fused_step", "essh_prefill_backward_workspace_bytes",
+            "essh_mixer_prefill_backward")
 
 
 class EsshLibraryMissing(RuntimeError):
@@ -89,6 +90,10 @@ def lib():
                                              + [P] * 11)
         L.essh_mixer_decode_step.restype = ctypes.c_int
         L.essh_mixer_decode_step.argtypes = [I32, ctypes.POINTER(Dims)] + [P] * 10 + [P]
+        L.essh_prefill_backward_workspace_bytes.restype = SZ
+        L.essh_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+        L.essh_mixer_prefill_backward.restype = ctypes.c_int
+        L.essh_mixer_prefill_backward.argtypes = [ctypes.POINTER(Dims)] + [P] * 21 + [SZ, P]
         _lib = L
     return _lib
 
@@ -174,6 +179,21 @@ def essh_mixer_decode_step(n_layers: int, dims: Dims, v, delta, g_w, g_r, rho, t
                                         _stream(stream))
 
 
+def essh_prefill_backward_workspace_bytes(dims: Dims) -> int:
+    return int(lib().essh_prefill_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def essh_mixer_prefill_backward(dims: Dims, v, delta, g_w, g_r, rho, theta, c, zl, state_in, dy, dstate_out,
+                                dv, ddelta, dg_w, dg_r, drho, dtheta, dc, dzl, dstate_in,
+                                workspace=None, workspace_bytes: int = 0, stream=None) -> int:
+    """Direct call of the prefill's backward pass; returns the status code."""
+    return lib().essh_mixer_prefill_backward(
+        ctypes.byref(dims), _ptr(v), _ptr(delta), _ptr(g_w), _ptr(g_r), _ptr(rho), _ptr(theta), _ptr(c), _ptr(zl),
+        _ptr(state_in), _ptr(dy), _ptr(dstate_out), _ptr(dv), _ptr(ddelta), _ptr(dg_w), _ptr(dg_r), _ptr(drho),
+        _ptr(dtheta), _ptr(dc), _ptr(dzl), _ptr(dstate_in), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
+
+
 # ---------------------------------------------------------------------------
 # Tensor-level helpers
 # ---------------------------------------------------------------------------
@@ -235,6 +255,45 @@ def prefill(v, delta, g_w, g_r, rho, theta, c, K_T=None, Lc=0, state_in=None, wa
     out = call.run()
     call.check()
     return out
+
+
+class PrefillBackward:
+    """A prepared backward call: dims, workspace and gradient buffers for fixed shapes.
+
+    Gradients of channels k >= K_T are left at zero (the library never writes them).  ``run``
+    only enqueues the library call."""
+
+    def __init__(self, v, delta, g_w, g_r, rho, theta, c, dy, K_T=None, state_in=None, dstate_out=None,
+                 zl=None, want_dzl=None, want_dstate_in=True, stream=None):
+        B, L, K, P = v.shape
+        m = rho.shape[1]
+        dev = v.device
+        self.dims = make_dims(B, L, K, m, P, K_T, 0, delta.dim() == 4, "bf16" if v.dtype == torch.bfloat16 else "f32")
+        self.args = (v, delta, g_w, g_r, rho, theta, c, zl, state_in, dy, dstate_out)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.grads = dict(
+            dv=torch.zeros_like(v), ddelta=torch.zeros(delta.shape, **f32), dg_w=torch.zeros(g_w.shape, **f32),
+            dg_r=torch.zeros(g_r.shape, **f32), drho=torch.zeros(rho.shape, **f32),
+            dtheta=torch.zeros(theta.shape, **f32), dc=torch.zeros(c.shape, **f32),
+            dzl=torch.zeros(rho.shape, **f32) if (zl is not None if want_dzl is None else want_dzl) else None,
+            dstate_in=torch.zeros((B, K, m, 2, P), **f32) if want_dstate_in else None)
+        self.ws_bytes = essh_prefill_backward_workspace_bytes(self.dims)
+        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev) if self.ws_bytes else None
+        self.stream = stream
+
+    def run(self):
+        g = self.grads
+        st = essh_mixer_prefill_backward(self.dims, *self.args, g["dv"], g["ddelta"], g["dg_w"], g["dg_r"],
+                                         g["drho"], g["dtheta"], g["dc"], g["dzl"], g["dstate_in"],
+                                         self.workspace, self.ws_bytes, self.stream)
+        _check(st, "essh_mixer_prefill_backward")
+        return g
+
+
+def prefill_backward(v, delta, g_w, g_r, rho, theta, c, dy, K_T=None, state_in=None, dstate_out=None, zl=None):
+    """Gradients of the prefill for dL/dy = dy (and dL/dstate_out = dstate_out).  Returns a dict
+    dv, ddelta, dg_w, dg_r, drho, dtheta, dc, dzl (None without zl), dstate_in."""
+    return PrefillBackward(v, delta, g_w, g_r, rho, theta, c, dy, K_T, state_in, dstate_out, zl).run()
 
 
 def decode_step(state, v, delta, g_w, g_r, rho, theta, c, K_T=None, y=None, zl=None):

@@ -155,6 +155,21 @@ def make_prefill_inputs(w: Workload, per_mode: bool = False, seed: Optional[int]
                 io=w.io, per_mode=per_mode)
 
 
+def make_backward_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Inputs of one backward call: the prefill inputs of ``w`` (per-channel controls), then
+    dy ~ N(0,1) [B,L,K,P] in the io dtype, state_in and dstate_out ~ N(0,1) [B,K,m,2,P] fp32 and
+    zero-lag coefficients zl ~ U(0,1) [K,m] fp32, drawn in that order."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    rho, theta, c = draw_params(rng, w.K, w.m, w.rho_lo, w.rho_hi)
+    v, delta, g_w, g_r = draw_tokens(rng, w.B, w.L, w.K, w.P, w.io, dna=w.dna)
+    dy = _io_array(rng.normal(0.0, 1.0, size=(w.B, w.L, w.K, w.P)), w.io)
+    state_in = rng.normal(0.0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    dstate_out = rng.normal(0.0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    zl = rng.uniform(0.0, 1.0, size=(w.K, w.m)).astype(np.float32)
+    return dict(v=v, delta=delta, g_w=g_w, g_r=g_r, rho=rho, theta=theta, c=c, dy=dy, state_in=state_in,
+                dstate_out=dstate_out, zl=zl, io=w.io, per_mode=False)
+
+
 def make_decode_inputs(w: Workload, n_steps: Optional[int] = None, context: Optional[int] = None,
                        seed: Optional[int] = None) -> dict:
     """Decode workload: per-layer params, a context to pre-fill the state, per-step tokens.
