@@ -334,6 +334,31 @@ def decode_fused_case(K_T, steps=20, warmup=3):
                 tflops=sizes.decode_fused_flops(NL, B, K_T, m, P, D) / (us * 1e-6) / 1e12)
 
 
+def backward_case(widx, K_T, steps, warmup):
+    """The backward pass of one prefill workload at tier K_T (entering state, zero-lag
+    coefficients and the final state's gradient all given): dy ~ N(0,1) and the extra inputs are
+    drawn on the GPU from a seeded generator."""
+    import torch
+    from selective_spectral_ssm_amd import essh, sizes
+    w, inp, d = workload_inputs(widx)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 1000)
+    B, L, K, P, m = w.B, w.L, w.K, w.P, w.m
+    dy = torch.randn(B, L, K, P, generator=g, device="cuda").to(d["v"].dtype)
+    s_in = torch.randn(B, K, m, 2, P, generator=g, device="cuda")
+    dso = torch.randn(B, K, m, 2, P, generator=g, device="cuda")
+    zl = torch.rand(K, m, generator=g, device="cuda")
+    call = essh.PrefillBackward(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], dy,
+                                K_T=K_T, state_in=s_in, dstate_out=dso, zl=zl)
+    ms_step, ms_launch, ms_med = time_launches(call.run, steps, warmup)
+    nbytes = sizes.backward_bytes(B, L, K_T, m, P, w.io)
+    return dict(workload=w.name, K_T=K_T, us_per_call=ms_launch * 1e3, us_per_call_median=ms_med * 1e3,
+                ms_per_step=ms_step, tokens_per_s=B * L / (ms_step * 1e-3), alg_bytes=nbytes,
+                achieved_GBs=nbytes / (ms_launch * 1e-3) / 1e9,
+                frac_of_hbm_peak=nbytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                workspace_MiB=call.ws_bytes / 2 ** 20)
+
+
 def _lscpu_model():
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
@@ -425,6 +450,8 @@ def main():
     ap.add_argument("--kt", type=int, default=HEADLINE[1], help="its tier K_T")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode at every tier (profiling runs); prints the decode JSON")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the prefill backward of --workload at --kt (profiling runs); prints its JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -448,6 +475,10 @@ def main():
         print(json.dumps({"decode_tiers": out, "decode_fused": fz}))
         return
     widx, KT = args.workload, args.kt
+    if args.backward_only:
+        log(f"backward: workload {widx} K_T={KT}")
+        print(json.dumps({"backward": backward_case(widx, KT, args.steps, args.warmup)}))
+        return
     wname = I.WORKLOADS[widx].name
     log(f"prefill: {wname} K_T={KT}")
     main_res, w, inp = prefill_case(widx, KT, args.steps, args.warmup)
@@ -530,6 +561,13 @@ def main():
                                              "frac_of_hbm_peak_kernel")})
             dt.append({k: res["decode"][k] for k in dt[0]})
             res["decode_tiers"] = dt
+    if not args.no_extra:
+        bw = []
+        for wi in (1, 2, 4):
+            kt = I.WORKLOADS[wi].tiers[-1]
+            log(f"prefill backward: workload {wi} K_T={kt}")
+            bw.append(backward_case(wi, kt, max(10, args.steps // 10), 3))
+        res["prefill_backward"] = bw
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, w, KT)

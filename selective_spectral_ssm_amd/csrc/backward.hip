@@ -53,15 +53,22 @@ constexpr int SB = 16;            // positions per sub-block
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float wave_sum64(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+// DPP lane moves within a row of 16 lanes (row_mask and bank_mask all on)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// sum over the 16 lanes of one row group (equal lane >> 4)
+constexpr int DPP_XOR1 = 0xb1;          // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4e;          // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane l of each 8-lane half reads lane 7 - l
+constexpr int DPP_MIRROR = 0x140;       // lane l of each row reads lane 15 - l
+
+// sum over the 16 lanes of one row group (equal lane >> 4); every lane gets the total
 __device__ __forceinline__ float row_sum16(float x) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 16);
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    x += dpp<DPP_MIRROR>(x);
     return x;
 }
 // sum over the four row groups (equal lane & 15)
@@ -70,6 +77,7 @@ __device__ __forceinline__ float group_sum4(float x) {
     x += __shfl_xor(x, 32);
     return x;
 }
+__device__ __forceinline__ float wave_sum64(float x) { return group_sum4(row_sum16(x)); }
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
@@ -104,21 +112,35 @@ __device__ void build_tables(Tables<M>& T, const BackwardArgs& a, int k, int lan
     __syncthreads();
 }
 
-// Controls of a sub-block: lane (g, i) holds position i (zeros past n) and the inclusive
-// clock sum q(i); qe = q(n - 1).
+// Controls of a sub-block: lane (g, i) holds position i (zeros past n), its inclusive clock
+// sum q(i) from the sub-block start, and qe = q(n - 1).
+struct CtlRegs {
+    float dl, gw, gr;
+};
 struct SubCtl {
     float gw, gr, q, qe;
 };
 
 template <typename IO>
-__device__ __forceinline__ SubCtl load_ctl(const BackwardArgs& a, int b, int k, int t0, int n, int i) {
+__device__ __forceinline__ CtlRegs load_ctl_regs(const BackwardArgs& a, int b, int k, int t0, int n, int i) {
     using io = io_traits<IO>;
+    CtlRegs c;
+    const bool in = i < n;
+    const size_t row = ((size_t)b * a.L + t0 + (in ? i : 0)) * a.K + k;   // clamped: always a valid address
+    const float dl = a.delta[row];
+    const float gw = io::load(static_cast<const IO*>(a.g_w), row);
+    const float gr = io::load(static_cast<const IO*>(a.g_r), row);
+    c.dl = in ? dl : 0.f;
+    c.gw = in ? gw : 0.f;
+    c.gr = in ? gr : 0.f;
+    return c;
+}
+
+__device__ __forceinline__ SubCtl finish_ctl(const CtlRegs& r, int n, int i) {
     SubCtl c;
-    const size_t row = ((size_t)b * a.L + t0 + (i < n ? i : 0)) * a.K + k;
-    const float dl = i < n ? a.delta[row] : 0.f;
-    c.gw = i < n ? io::load(static_cast<const IO*>(a.g_w), row) : 0.f;
-    c.gr = i < n ? io::load(static_cast<const IO*>(a.g_r), row) : 0.f;
-    float q = dl;
+    c.gw = r.gw;
+    c.gr = r.gr;
+    float q = r.dl;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
         const float o = __shfl_up(q, off, 16);
@@ -129,36 +151,71 @@ __device__ __forceinline__ SubCtl load_ctl(const BackwardArgs& a, int b, int k, 
     return c;
 }
 
-// Rows [0, n) of a [16][NTC] tile of an io-dtype array with row stride `stride` elements, into
-// LDS rows of LD floats (rows n..15 zero).  16-byte loads.
-template <typename IO, int NTC, int LD>
-__device__ __forceinline__ void load_tile(float* tile, const IO* src, size_t stride, int n, int lane) {
-    constexpr int E = 16 / sizeof(IO);
-    constexpr int CPR = NTC / E;
-    for (int idx = lane; idx < SB * CPR; idx += 64) {
-        const int r = idx / CPR, col = (idx - r * CPR) * E;
-        float x[E];
-        if (r < n) {
-            const uint4 w = *reinterpret_cast<const uint4*>(src + r * stride + col);
-            if constexpr (E == 8) {
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+// Rows [0, n) of a [16][NTC] tile of an io-dtype array (row stride `stride` elements), loaded
+// with 16-byte loads into registers (rows n..15 as zeros) and later stored into LDS rows of LD
+// floats; and the reverse direction for an output tile.
+template <typename IO, int NTC>
+struct TileRegs {
+    static constexpr int E = 16 / sizeof(IO);         // elements per 16-byte chunk
+    static constexpr int CPR = NTC / E;               // chunks per row
+    static constexpr int NCH = SB * CPR;              // chunks per tile
+    static constexpr int PER = (NCH + 63) / 64;       // chunks per lane
+    uint4 x[PER];
+
+    __device__ __forceinline__ void load(const IO* src, size_t stride, int n, int lane) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[2 * e] = __uint_as_float(u[e] << 16);
-                    x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-                }
-            } else {
-                x[0] = __uint_as_float(w.x);
-                x[1] = __uint_as_float(w.y);
-                x[2] = __uint_as_float(w.z);
-                x[3] = __uint_as_float(w.w);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = 0.f;
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + 64 * e;
+            const int r = idx / CPR, col = (idx - r * CPR) * E;
+            const bool ok = (NCH % 64 == 0 || idx < NCH) && r < n;
+            const int rr = ok ? r : 0, cc = ok ? col : 0;   // clamped: always a valid address
+            const uint4 w = *reinterpret_cast<const uint4*>(src + rr * stride + cc);
+            x[e] = ok ? w : make_uint4(0u, 0u, 0u, 0u);
         }
+    }
+    template <int LD>
+    __device__ __forceinline__ void store(float* tile, int lane) const {
 #pragma unroll
-        for (int e = 0; e < E; ++e) tile[r * LD + col + e] = x[e];
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + 64 * e;
+            if (NCH % 64 == 0 || idx < NCH) {
+                const int r = idx / CPR, col = (idx - r * CPR) * E;
+                float* d = tile + r * LD + col;
+                if constexpr (E == 8) {
+                    *reinterpret_cast<float4*>(d) = make_float4(__uint_as_float(x[e].x << 16),
+                                                                __uint_as_float(x[e].x & 0xffff0000u),
+                                                                __uint_as_float(x[e].y << 16),
+                                                                __uint_as_float(x[e].y & 0xffff0000u));
+                    *reinterpret_cast<float4*>(d + 4) = make_float4(__uint_as_float(x[e].z << 16),
+                                                                    __uint_as_float(x[e].z & 0xffff0000u),
+                                                                    __uint_as_float(x[e].w << 16),
+                                                                    __uint_as_float(x[e].w & 0xffff0000u));
+                } else {
+                    *reinterpret_cast<float4*>(d) = make_float4(__uint_as_float(x[e].x), __uint_as_float(x[e].y),
+                                                                __uint_as_float(x[e].z), __uint_as_float(x[e].w));
+                }
+            }
+        }
+    }
+};
+
+template <typename IO, int NTC, int LD>
+__device__ __forceinline__ void store_out_tile(IO* dst, size_t stride, int n, const float* tile, int lane) {
+    constexpr int E = 16 / sizeof(IO), CPR = NTC / E, NCH = SB * CPR;
+    for (int idx = lane; idx < NCH; idx += 64) {
+        const int r = idx / CPR, col = (idx - r * CPR) * E;
+        if (r >= n) continue;
+        const float* s = tile + r * LD + col;
+        uint4 w;
+        if constexpr (E == 8) {
+            w.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
+            w.y = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
+            w.z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
+            w.w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
+        } else {
+            w = make_uint4(__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3]));
+        }
+        *reinterpret_cast<uint4*>(dst + r * stride + col) = w;
     }
 }
 
@@ -184,19 +241,29 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
     const int s0 = seg * pl.Ls, len = min(pl.Ls, a.L - s0), nsb = (len + SB - 1) / SB;
     const int col0 = sl * NTC;
     const size_t rs = (size_t)a.K * pl.P;
-    build_tables<M>(T, a, k, lane);
     const size_t segi = (size_t)seq * pl.nseg + seg;
+    const IO* vsrc = static_cast<const IO*>(a.v) + (((size_t)b * a.L) * a.K + k) * pl.P + col0;
+    const IO* dsrc = static_cast<const IO*>(a.dy) + (((size_t)b * a.L) * a.K + k) * pl.P + col0;
+    auto sub_n = [&](int sb) { return min(SB, s0 + len - (s0 + sb * SB)); };
+    build_tables<M>(T, a, k, lane);
 
     // local state chain from zero; checkpoint after every sub-block
     f32x4 st[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float2 tr0 = make_float2(1.f, 0.f), tr1 = make_float2(1.f, 0.f);
+    CtlRegs cr = load_ctl_regs<IO>(a, b, k, s0, sub_n(0), i);
+    TileRegs<IO, NTC> tv;
+    tv.load(vsrc + (size_t)s0 * rs, rs, sub_n(0), lane);
     for (int sb = 0; sb < nsb; ++sb) {
-        const int t0 = s0 + sb * SB, n = min(SB, s0 + len - t0);
-        const SubCtl c = load_ctl<IO>(a, b, k, t0, n, i);
-        load_tile<IO, NTC, LD>(tile, static_cast<const IO*>(a.v) + (((size_t)b * a.L + t0) * a.K + k) * pl.P + col0,
-                               rs, n, lane);
+        const int n = sub_n(sb);
+        const SubCtl c = finish_ctl(cr, n, i);
+        tv.template store<LD>(tile, lane);
+        if (sb + 1 < nsb) {
+            const int t1 = s0 + (sb + 1) * SB;
+            cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb + 1), i);
+            tv.load(vsrc + (size_t)t1 * rs, rs, sub_n(sb + 1), lane);
+        }
         float wa[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -244,11 +311,20 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
     f32x4 bt[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bt[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        const int t1 = s0 + (nsb - 1) * SB;
+        cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(nsb - 1), i);
+        tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(nsb - 1), lane);
+    }
     for (int sb = nsb - 1; sb >= 0; --sb) {
-        const int t0 = s0 + sb * SB, n = min(SB, s0 + len - t0);
-        const SubCtl c = load_ctl<IO>(a, b, k, t0, n, i);
-        load_tile<IO, NTC, LD>(tile, static_cast<const IO*>(a.dy) + (((size_t)b * a.L + t0) * a.K + k) * pl.P + col0,
-                               rs, n, lane);
+        const int n = sub_n(sb);
+        const SubCtl c = finish_ctl(cr, n, i);
+        tv.template store<LD>(tile, lane);
+        if (sb > 0) {
+            const int t1 = s0 + (sb - 1) * SB;
+            cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb - 1), i);
+            tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(sb - 1), lane);
+        }
         float ca[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -285,8 +361,11 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
 }
 
 // ------------------------------------------------------------------------------------------
-// 2. scan over segments: one thread per (sequence, mode, value column)
+// 2. scan over segments: one thread per (sequence, mode, value column); loads go out in
+//    batches ahead of the dependent chain
 // ------------------------------------------------------------------------------------------
+constexpr int SCAN_BATCH = 8;
+
 template <int M>
 __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan pl) {
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -298,41 +377,76 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan p
     const int k = seq % a.K_T, b = seq / a.K_T;
     constexpr int ROWS = 2 * M;
     const size_t sidx = ((((size_t)b * a.K + k) * M + j) * 2) * P + p;   // state [B][K][m][2][P]
+    const size_t seg0 = (size_t)seq * pl.nseg;
 
     float hr = 0.f, hi = 0.f;
     if (a.state_in) {
         hr = a.state_in[sidx];
         hi = a.state_in[sidx + P];
     }
-    for (int seg = 0; seg < pl.nseg; ++seg) {
-        const size_t segi = (size_t)seq * pl.nseg + seg;
-        float* hin = pl.hin + (segi * ROWS + 2 * j) * (size_t)P + p;
-        hin[0] = hr;
-        hin[P] = hi;
-        const int len = min(pl.Ls, a.L - seg * pl.Ls), nsb = (len + SB - 1) / SB;
-        const float* agg = pl.ck + ((segi * pl.nsb + nsb - 1) * ROWS + 2 * j) * (size_t)P + p;
-        const float2 t = pl.lam[segi * M + j];
-        const float nr = t.x * hr - t.y * hi + agg[0];
-        const float ni = t.y * hr + t.x * hi + agg[P];
-        hr = nr;
-        hi = ni;
+    for (int sbase = 0; sbase < pl.nseg; sbase += SCAN_BATCH) {
+        float ar[SCAN_BATCH], ai[SCAN_BATCH];
+        float2 t[SCAN_BATCH];
+#pragma unroll
+        for (int q = 0; q < SCAN_BATCH; ++q) {
+            const int seg = sbase + q;
+            ar[q] = ai[q] = 0.f;
+            t[q] = make_float2(0.f, 0.f);
+            if (seg < pl.nseg) {
+                const int len = min(pl.Ls, a.L - seg * pl.Ls), nsb = (len + SB - 1) / SB;
+                const float* agg = pl.ck + (((seg0 + seg) * pl.nsb + nsb - 1) * ROWS + 2 * j) * (size_t)P + p;
+                ar[q] = agg[0];
+                ai[q] = agg[P];
+                t[q] = pl.lam[(seg0 + seg) * M + j];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < SCAN_BATCH; ++q) {
+            const int seg = sbase + q;
+            if (seg < pl.nseg) {
+                float* hin = pl.hin + ((seg0 + seg) * ROWS + 2 * j) * (size_t)P + p;
+                hin[0] = hr;
+                hin[P] = hi;
+                const float nr = t[q].x * hr - t[q].y * hi + ar[q];
+                const float ni = t[q].y * hr + t[q].x * hi + ai[q];
+                hr = nr;
+                hi = ni;
+            }
+        }
     }
     float br = 0.f, bi = 0.f;
     if (a.dstate_out) {
         br = a.dstate_out[sidx];
         bi = a.dstate_out[sidx + P];
     }
-    for (int seg = pl.nseg - 1; seg >= 0; --seg) {
-        const size_t segi = (size_t)seq * pl.nseg + seg;
-        float* sa = pl.sa + (segi * ROWS + 2 * j) * (size_t)P + p;
-        const float ar = sa[0], ai = sa[P];
-        sa[0] = br;   // arriving adjoint of this segment
-        sa[P] = bi;
-        const float2 t = pl.lam[segi * M + j];
-        const float nr = t.x * br + t.y * bi + ar;
-        const float ni = t.x * bi - t.y * br + ai;
-        br = nr;
-        bi = ni;
+    for (int stop = pl.nseg; stop > 0; stop -= SCAN_BATCH) {
+        float ar[SCAN_BATCH], ai[SCAN_BATCH];
+        float2 t[SCAN_BATCH];
+#pragma unroll
+        for (int q = 0; q < SCAN_BATCH; ++q) {
+            const int seg = stop - 1 - q;
+            ar[q] = ai[q] = 0.f;
+            t[q] = make_float2(0.f, 0.f);
+            if (seg >= 0) {
+                const float* sa = pl.sa + ((seg0 + seg) * ROWS + 2 * j) * (size_t)P + p;
+                ar[q] = sa[0];
+                ai[q] = sa[P];
+                t[q] = pl.lam[(seg0 + seg) * M + j];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < SCAN_BATCH; ++q) {
+            const int seg = stop - 1 - q;
+            if (seg >= 0) {
+                float* sa = pl.sa + ((seg0 + seg) * ROWS + 2 * j) * (size_t)P + p;
+                sa[0] = br;   // arriving adjoint of this segment
+                sa[P] = bi;
+                const float nr = t[q].x * br + t[q].y * bi + ar[q];
+                const float ni = t[q].x * bi - t[q].y * br + ai[q];
+                br = nr;
+                bi = ni;
+            }
+        }
     }
     if (a.dstate_in) {
         a.dstate_in[sidx] = br;
@@ -344,16 +458,20 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan p
 // 3. gradients of every sub-block
 // ------------------------------------------------------------------------------------------
 template <int M, int NTC, typename IO>
-__global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl) {
-    constexpr int NT = NTC / 16, ROWS = 2 * M, KR = (ROWS + 3) / 4, LD = NTC + 4, KS = NTC / 4;
+__global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan pl) {
+    constexpr int NT = NTC / 16, ROWS = 2 * M, KR = (ROWS + 3) / 4, LD = NTC + 4, KS = NTC / 4, LM = SB + 1;
+    constexpr int CKN = M * NTC, CKE = (CKN + 63) / 64;   // complex state entries, per lane
     __shared__ Tables<M> T;
-    __shared__ float vt[SB * LD], dyt[SB * LD], dvo[SB * LD];
-    __shared__ float hbuf[2][SB * LD];     // state at the sub-block's start, and at its end
-    __shared__ float b1m[SB * LD];         // arriving adjoint, [row][column]
-    __shared__ float hin[ROWS * LD];       // the segment's entering state
+    __shared__ float vt[SB * LD], dyt[SB * LD];   // v tile (then the dv tile) and dy tile
+    __shared__ float hbuf[2][SB * LD];            // states entering the sub-block and leaving it
+    __shared__ float hin[ROWS * LD];              // the segment's entering state
+    __shared__ float b1m[SB * LD];                // adjoint arriving at the sub-block's end
     __shared__ float2 tpref[MAX_BWD_SUBBLOCKS + 1][M];
+    __shared__ float pos[5][SB];                  // q, g_r, g_w, e^{-q}, e^{-(q(n-1) - q)}
+    __shared__ float GT[SB * LM];                 // [s][u] = g_r(u) e^{-(q(u)-q(s))} psi(u - s), u >= s
+    __shared__ float WQ[SB * LM];                 // [u][row] = e^{-q(u)} {Re, -Im}(c_j lambda_j^{u+1})
+    __shared__ float WT[SB * LM];                 // [s][row] = e^{-(q(n-1)-q(s))} {Re, Im}(lambda_j^{n-1-s})
     __shared__ float red[4][SB];
-    using io = io_traits<IO>;
 
     const int lane = threadIdx.x, i = lane & 15, g = lane >> 4;
     const int seg = blockIdx.x, sl = blockIdx.y, seq = blockIdx.z;
@@ -362,17 +480,22 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
     const int col0 = sl * NTC, P = pl.P;
     const size_t rs = (size_t)a.K * P;
     const size_t segi = (size_t)seq * pl.nseg + seg;
+    const size_t rowb = ((size_t)b * a.L) * a.K + k;      // control index of position 0
+    const IO* vsrc = static_cast<const IO*>(a.v) + rowb * P + col0;
+    const IO* dsrc = static_cast<const IO*>(a.dy) + rowb * P + col0;
+    auto sub_n = [&](int sb) { return min(SB, s0 + len - (s0 + sb * SB)); };
     build_tables<M>(T, a, k, lane);
 
-    // rows >= 2m of the LDS states stay zero; entering state; arriving adjoint
-    for (int idx = lane; idx < SB * LD; idx += 64) {
-        hbuf[0][idx] = 0.f;
-        hbuf[1][idx] = 0.f;
-        b1m[idx] = 0.f;
-    }
     for (int idx = lane; idx < ROWS * NTC; idx += 64) {
         const int r = idx / NTC, col = idx - r * NTC;
         hin[r * LD + col] = pl.hin[(segi * ROWS + r) * (size_t)P + col0 + col];
+    }
+    // rows 2m..15 of the state and adjoint buffers stay zero, so that they can be read as
+    // operands without a bound check
+    for (int idx = ROWS * LD + lane; idx < SB * LD; idx += 64) {
+        hbuf[0][idx] = 0.f;
+        hbuf[1][idx] = 0.f;
+        b1m[idx] = 0.f;
     }
     if (lane < M) {   // transfer from the segment start to the start of every sub-block
         float2 t = make_float2(1.f, 0.f);
@@ -382,7 +505,6 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
             tpref[sb + 1][lane] = t;
         }
     }
-    __syncthreads();
     f32x4 b1[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -394,124 +516,190 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
             b1m[row * LD + nt * 16 + i] = x;
         }
 
-    // true state after sub-block sb - 1 (sb = 0: the entering state): local checkpoint plus the
-    // entering state carried by the transfer from the segment start
-    auto build_state = [&](float* dst, int sb) {
-        for (int idx = lane; idx < M * NTC; idx += 64) {
-            const int j = idx / NTC, col = idx - j * NTC;
-            float lr = 0.f, li = 0.f;
-            if (sb > 0) {
-                const float* ck = pl.ck + ((segi * pl.nsb + sb - 1) * ROWS + 2 * j) * (size_t)P + col0 + col;
-                lr = ck[0];
-                li = ck[P];
-            }
-            const float2 t = tpref[sb][j];
-            const float hr = hin[2 * j * LD + col], hi = hin[(2 * j + 1) * LD + col];
-            dst[2 * j * LD + col] = lr + t.x * hr - t.y * hi;
-            dst[(2 * j + 1) * LD + col] = li + t.x * hi + t.y * hr;
+    // local checkpoint after sub-block sb - 1 (zero for sb = 0), at this lane's entries
+    auto load_ck = [&](float2 (&ckr)[CKE], int sb) {
+#pragma unroll
+        for (int e = 0; e < CKE; ++e) {
+            const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
+            const bool ok = sb > 0 && (CKN % 64 == 0 || idx < CKN);
+            const int sc = ok ? sb - 1 : 0, jc = ok ? j : 0, cc = ok ? col : 0;   // clamped address
+            const float* ck = pl.ck + ((segi * pl.nsb + sc) * ROWS + 2 * jc) * (size_t)P + col0 + cc;
+            const float xr = ck[0], xi = ck[P];
+            ckr[e] = ok ? make_float2(xr, xi) : make_float2(0.f, 0.f);
         }
     };
+    // true state entering sub-block sb: the checkpoint plus the segment's entering state
+    // carried by the transfer from the segment start
+    auto put_state = [&](float* hs, const float2 (&ckr)[CKE], int sb) {
+#pragma unroll
+        for (int e = 0; e < CKE; ++e) {
+            const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
+            if (CKN % 64 == 0 || idx < CKN) {
+                const float2 t = tpref[sb][j];
+                const float hr = hin[2 * j * LD + col], hi = hin[(2 * j + 1) * LD + col];
+                hs[2 * j * LD + col] = ckr[e].x + t.x * hr - t.y * hi;
+                hs[(2 * j + 1) * LD + col] = ckr[e].y + t.x * hi + t.y * hr;
+            }
+        }
+    };
+    // a state's entry of result-layout register r of tile nt (rows >= 2m read as zero)
+    auto st_at = [&](const float* hs, int nt, int r) { return hs[(4 * g + r) * LD + nt * 16 + i]; };
+
+    __syncthreads();
+    int cur = 0;   // hbuf[cur]: state leaving the sub-block being processed
+    {
+        float2 ckr[CKE];
+        load_ck(ckr, nsb);
+        put_state(hbuf[cur], ckr, nsb);
+    }
+    float2 ckn[CKE];
+    CtlRegs crn;
+    TileRegs<IO, NTC> tvn, tdn;
+    {
+        const int t1 = s0 + (nsb - 1) * SB, n1 = sub_n(nsb - 1);
+        load_ck(ckn, nsb - 1);
+        crn = load_ctl_regs<IO>(a, b, k, t1, n1, i);
+        tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
+        tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
+    }
+    __syncthreads();
 
     f32x4 nacc = f32x4{0.f, 0.f, 0.f, 0.f}, qacc = nacc, racc = nacc;
     float2 zc0 = make_float2(0.f, 0.f), zc1 = zc0;    // modes 2g, 2g + 1
-    int cur = 0;                                       // hbuf[cur] = state at the end of sub-block sb
-    build_state(hbuf[cur], nsb);
 
     for (int sb = nsb - 1; sb >= 0; --sb) {
-        const int t0 = s0 + sb * SB, n = min(SB, s0 + len - t0);
-        const SubCtl c = load_ctl<IO>(a, b, k, t0, n, i);
-        float* hn = hbuf[cur];
-        float* h0 = hbuf[cur ^ 1];
-        build_state(h0, sb);
-        const size_t row0 = ((size_t)b * a.L + t0) * a.K + k;
-        load_tile<IO, NTC, LD>(vt, static_cast<const IO*>(a.v) + row0 * P + col0, rs, n, lane);
-        load_tile<IO, NTC, LD>(dyt, static_cast<const IO*>(a.dy) + row0 * P + col0, rs, n, lane);
+        const int t0 = s0 + sb * SB, n = sub_n(sb);
+        const SubCtl c = finish_ctl(crn, n, i);
+        tvn.template store<LD>(vt, lane);
+        tdn.template store<LD>(dyt, lane);
+        float* hs = hbuf[cur ^ 1];     // state entering this sub-block
+        const float* hn = hbuf[cur];   // state leaving it
+        put_state(hs, ckn, sb);
+        if (g == 0) {
+            pos[0][i] = c.q;
+            pos[1][i] = c.gr;
+            pos[2][i] = c.gw;
+            pos[3][i] = i < n ? expf(-c.q) : 0.f;
+            pos[4][i] = i < n ? expf(c.q - c.qe) : 0.f;
+        }
+        if (sb > 0) {   // inputs of the next sub-block (the one before) go out now
+            const int t1 = t0 - SB, n1 = sub_n(sb - 1);
+            load_ck(ckn, sb - 1);
+            crn = load_ctl_regs<IO>(a, b, k, t1, n1, i);
+            tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
+            tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
+        }
+        __syncthreads();
+
+        // ---- the sub-block's operand matrices; lane (g, i) fills entries (4 g + r, i) ----
+        float eS[4];   // e^{-(q(u) - q(s))} at (u = 4 g + r, s = i), u >= s
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int aa = 4 * g + r;
+            const float qa = pos[0][aa];
+            eS[r] = (aa >= i && aa < n) ? expf(c.q - qa) : 0.f;
+            GT[aa * LM + i] = (i >= aa && i < n) ? c.gr * expf(qa - c.q) * T.psi[i >= aa ? i - aa : 0] : 0.f;
+            const bool rok = i < ROWS;
+            const int jj = rok ? i >> 1 : 0;
+            const float2 cp = T.cpw[aa + 1][jj];
+            const float2 p = T.pw[aa < n ? n - 1 - aa : 0][jj];
+            const float wq = pos[3][aa] * ((i & 1) ? -cp.y : cp.x);
+            const float wt = pos[4][aa] * ((i & 1) ? p.y : p.x);
+            WQ[aa * LM + i] = rok ? wq : 0.f;
+            WT[aa * LM + i] = rok ? wt : 0.f;
+        }
         __syncthreads();
 
         // ---- products over the value columns: S = dY V^T, Q = dY H0^T, R = V_rev B1^T ----
         f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f}, Q = S, R = S;
-        const int ir = n - 1 - i;   // reversed row of V for R
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int col = g * KS + kk;
-            const float dya = dyt[i * LD + col];
-            S = mfma4(dya, vt[i * LD + col], S);
-            Q = mfma4(dya, h0[i * LD + col], Q);
-            R = mfma4(ir >= 0 ? vt[ir * LD + col] : 0.f, b1m[i * LD + col], R);
+        {
+            const int ir = i < n ? n - 1 - i : SB - 1;   // reversed row of V for R (row 15 is zero when n < 16)
+            // four columns per 16-byte LDS read; one group at a time keeps few operands live
+#pragma unroll 1
+            for (int k4 = 0; k4 < KS; k4 += 4) {
+                const int col = g * KS + k4;
+                const float4 d4 = *reinterpret_cast<const float4*>(dyt + i * LD + col);
+                const float4 v4 = *reinterpret_cast<const float4*>(vt + i * LD + col);
+                const float4 h4 = *reinterpret_cast<const float4*>(hs + i * LD + col);
+                const float4 r4 = *reinterpret_cast<const float4*>(vt + ir * LD + col);
+                const float4 b4 = *reinterpret_cast<const float4*>(b1m + i * LD + col);
+                S = mfma4(d4.x, v4.x, S);
+                Q = mfma4(d4.x, h4.x, Q);
+                R = mfma4(r4.x, b4.x, R);
+                S = mfma4(d4.y, v4.y, S);
+                Q = mfma4(d4.y, h4.y, Q);
+                R = mfma4(r4.y, b4.y, R);
+                S = mfma4(d4.z, v4.z, S);
+                Q = mfma4(d4.z, h4.z, Q);
+                R = mfma4(r4.z, b4.z, R);
+                S = mfma4(d4.w, v4.w, S);
+                Q = mfma4(d4.w, h4.w, Q);
+                R = mfma4(r4.w, b4.w, R);
+            }
         }
 
         // ---- S: intra-sub-block sums for dg_r and dg_w, and the N accumulator ----
-        float dgw_col = 0.f;
+        float dgw_col = 0.f, rsel = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int u = 4 * g + r;
-            const float qu = __shfl(c.q, u, 16), gru = __shfl(c.gr, u, 16);
-            const bool ok = u >= i && u < n;
-            const float e = ok ? expf(c.q - qu) : 0.f;
-            const float x = ok ? e * T.psi[u - i] * S[r] : 0.f;
+            const float gru = pos[1][u];
+            const float x = eS[r] * T.psi[u >= i ? u - i : 0] * S[r];
             const float rsum = row_sum16(c.gw * x);
-            if (i == r) red[0][u] = rsum;
+            rsel = i == r ? rsum : rsel;
             dgw_col += gru * x;
-            nacc[r] += ok ? gru * c.gw * e * S[r] : 0.f;
+            nacc[r] += gru * c.gw * eS[r] * S[r];
         }
         dgw_col = group_sum4(dgw_col);
+        if (i < 4) red[0][4 * g + i] = rsel;
         if (g == 0) red[2][i] = dgw_col;
 
         // ---- Q: carried-state part of dg_r; R: end-state part of dg_w ----
+        float qsel = 0.f, esel = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int u = 4 * g + r;
-            const float qu = __shfl(c.q, u, 16), gru = __shfl(c.gr, u, 16);
-            const bool okq = u < n && i < ROWS;
-            float wq = 0.f, eq = 0.f;
-            if (okq) {
-                const float2 cp = T.cpw[u + 1][i >> 1];
-                eq = expf(-qu);
-                wq = eq * ((i & 1) ? -cp.y : cp.x);
-            }
-            const float cs = row_sum16(wq * Q[r]);
-            if (i == r) red[1][u] = cs;
-            qacc[r] += okq ? gru * eq * Q[r] : 0.f;
-
-            const int sp = u, s = n - 1 - sp;     // R row sp is position s
-            const float qs = __shfl(c.q, s < 0 ? 0 : s, 16), gws = __shfl(c.gw, s < 0 ? 0 : s, 16);
-            const bool okr = sp < n && i < ROWS;
-            float wr = 0.f, er = 0.f;
-            if (okr) {
-                const float2 p = T.pw[sp][i >> 1];
-                er = expf(qs - c.qe);
-                wr = er * ((i & 1) ? p.y : p.x);
-            }
+            const float cs = row_sum16(WQ[u * LM + i] * Q[r]);
+            qsel = i == r ? cs : qsel;
+            qacc[r] += pos[1][u] * pos[3][u] * Q[r];
+            const int s = n - 1 - u;      // R row u is position s
+            const int sc = s >= 0 ? s : 0;
+            const float wt_ = WT[sc * LM + i];
+            const float wr = s >= 0 ? wt_ : 0.f;
             const float es = row_sum16(wr * R[r]);
-            if (i == r && sp < n) red[3][s] = es;
-            racc[r] += okr ? er * gws * R[r] : 0.f;
+            esel = i == r ? es : esel;
+            const float rw = pos[4][sc] * pos[2][sc];
+            racc[r] += s >= 0 ? rw * R[r] : 0.f;
+        }
+        if (i < 4) {
+            red[1][4 * g + i] = qsel;
+            const int s = n - 1 - (4 * g + i);
+            if (s >= 0) red[3][s] = esel;
         }
 
         // ---- inner products of the arriving adjoint with the end and entering states ----
         float xe = 0.f, z0r = 0.f, z0i = 0.f, z1r = 0.f, z1i = 0.f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int col = nt * 16 + i;
-            float he[4], hs[4];
+            float h0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                he[r] = hn[(4 * g + r) * LD + col];
-                hs[r] = h0[(4 * g + r) * LD + col];
-                xe += b1[nt][r] * he[r];
+                xe += b1[nt][r] * st_at(hn, nt, r);
+                h0[r] = st_at(hs, nt, r);
             }
-            z0r += b1[nt][0] * hs[0] + b1[nt][1] * hs[1];
-            z0i += b1[nt][0] * hs[1] - b1[nt][1] * hs[0];
-            z1r += b1[nt][2] * hs[2] + b1[nt][3] * hs[3];
-            z1i += b1[nt][2] * hs[3] - b1[nt][3] * hs[2];
+            z0r += b1[nt][0] * h0[0] + b1[nt][1] * h0[1];
+            z0i += b1[nt][0] * h0[1] - b1[nt][1] * h0[0];
+            z1r += b1[nt][2] * h0[2] + b1[nt][3] * h0[3];
+            z1i += b1[nt][2] * h0[3] - b1[nt][3] * h0[2];
         }
         xe = wave_sum64(xe);
         z0r = row_sum16(z0r);
         z0i = row_sum16(z0i);
         z1r = row_sum16(z1r);
         z1i = row_sum16(z1i);
+        const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
         {
             // n lambda_j^n e^{-q(n-1)} conj(B1_j) . H0_j, accumulated per mode
-            const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
             const float2 a0 = cmul(l0, make_float2(z0r, z0i)), a1 = cmul(l1, make_float2(z1r, z1i));
             zc0.x += (float)n * a0.x;
             zc0.y += (float)n * a0.y;
@@ -532,7 +720,7 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
             }
             const float ddl = cs - xe;
             if (g == 0 && i < n) {
-                const size_t ci = row0 + (size_t)i * a.K;
+                const size_t ci = rowb + (size_t)(t0 + i) * a.K;
                 if (pl.nslice == 1) {
                     a.ddelta[ci] = ddl;
                     a.dg_w[ci] = dgw;
@@ -546,26 +734,13 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
             }
         }
 
-        // ---- dv = g_w (G^T dY + W^T B1) ----
+        // ---- dv = g_w (G^T dY + W^T B1), staged in the v tile ----
         {
             float ga[4], wt[KR];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int u = 4 * kk + g;
-                const float qu = __shfl(c.q, u, 16), gru = __shfl(c.gr, u, 16);
-                ga[kk] = (u >= i && u < n) ? gru * expf(c.q - qu) * T.psi[u - i] : 0.f;
-            }
-            const float ew = i < n ? expf(c.q - c.qe) : 0.f;
+            for (int kk = 0; kk < 4; ++kk) ga[kk] = GT[i * LM + 4 * kk + g];
 #pragma unroll
-            for (int kk = 0; kk < KR; ++kk) {
-                const int row = 4 * kk + g;
-                float w = 0.f;
-                if (i < n && row < ROWS) {
-                    const float2 p = T.pw[n - 1 - i][row >> 1];
-                    w = ew * ((row & 1) ? p.y : p.x);
-                }
-                wt[kk] = w;
-            }
+            for (int kk = 0; kk < KR; ++kk) wt[kk] = WT[i * LM + 4 * kk + g];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int col = nt * 16 + i;
@@ -573,17 +748,11 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) d = mfma4(ga[kk], dyt[(4 * kk + g) * LD + col], d);
 #pragma unroll
-                for (int kk = 0; kk < KR; ++kk) d = mfma4(wt[kk], b1m[(4 * kk + g) * LD + col], d);
+                for (int kk = 0; kk < KR; ++kk) {
+                    d = mfma4(wt[kk], b1m[(4 * kk + g) * LD + col], d);
+                }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dvo[(4 * g + r) * LD + col] = __shfl(c.gw, 4 * g + r, 16) * d[r];
-            }
-        }
-        __syncthreads();
-        {
-            IO* dv = static_cast<IO*>(a.dv) + row0 * P + col0;
-            for (int idx = lane; idx < SB * NTC; idx += 64) {
-                const int r = idx / NTC, col = idx - r * NTC;
-                if (r < n) io::store(dv, (size_t)r * rs + col, dvo[r * LD + col]);
+                for (int r = 0; r < 4; ++r) vt[(4 * g + r) * LD + col] = pos[2][4 * g + r] * d[r];
             }
         }
 
@@ -593,15 +762,8 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int u = 4 * kk + g;
-                const float qu = __shfl(c.q, u, 16), gru = __shfl(c.gr, u, 16);
-                float w = 0.f;
-                if (i < ROWS && u < n) {
-                    const float2 cp = T.cpw[u + 1][i >> 1];
-                    w = gru * expf(-qu) * ((i & 1) ? -cp.y : cp.x);
-                }
-                ca[kk] = w;
+                ca[kk] = pos[1][u] * WQ[u * LM + i];   // columns >= 2m of WQ are zero
             }
-            const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 f32x4 d;
@@ -614,13 +776,14 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
                 b1[nt] = d;
             }
         }
-        __syncthreads();   // every read of b1m, vt, dyt and dvo of this sub-block is done
+        __syncthreads();   // every read of b1m, vt (as v) and dyt of this sub-block is done
+        store_out_tile<IO, NTC, LD>(static_cast<IO*>(a.dv) + (rowb + (size_t)t0 * a.K) * P + col0, rs, n, vt, lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r < ROWS) b1m[(4 * g + r) * LD + nt * 16 + i] = b1[nt][r];
+            for (int r = 0; r < 4; ++r) b1m[(4 * g + r) * LD + nt * 16 + i] = b1[nt][r];   // rows >= 2m are zero
         cur ^= 1;
+        __syncthreads();
     }
 
     // ---- mode-table partials of this segment ----
@@ -697,24 +860,29 @@ __global__ void __launch_bounds__(64) bwd_grad_kernel(BackwardArgs a, BwdPlan pl
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. mode-table gradients: sums of the partials over batch rows, segments and slices
+// 4. mode-table gradients: sums of the partials over batch rows, segments and slices (one
+//    workgroup per channel; each wave sums some of the 4m + 1 quantities)
 // ------------------------------------------------------------------------------------------
 template <int M>
-__global__ void __launch_bounds__(64) bwd_param_kernel(BackwardArgs a, BwdPlan pl) {
-    const int k = blockIdx.x, lane = threadIdx.x;
+__global__ void __launch_bounds__(256) bwd_param_kernel(BackwardArgs a, BwdPlan pl) {
+    const int k = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int W = 4 * M + 1;
     __shared__ float tot[W];
-    if (lane < W) {
+    const int per = pl.nseg * pl.nslice;
+    const int count = a.B * per;
+    for (int w = wave; w < W; w += 4) {
         float s = 0.f;
-        for (int b = 0; b < a.B; ++b) {
+        for (int e = lane; e < count; e += 64) {
+            const int b = e / per, r = e - b * per;
             const size_t seq = (size_t)b * a.K_T + k;
-            for (int e = 0; e < pl.nseg * pl.nslice; ++e) s += pl.pp[(seq * pl.nseg * pl.nslice + e) * W + lane];
+            s += pl.pp[(seq * per + r) * W + w];
         }
-        tot[lane] = s;
+        s = wave_sum64(s);
+        if (lane == 0) tot[w] = s;
     }
     __syncthreads();
-    if (lane < M) {
-        const int j = lane;
+    if (threadIdx.x < M) {
+        const int j = threadIdx.x;
         const float tr = tot[4 * M];
         const size_t kj = (size_t)k * M + j;
         a.drho[kj] = tot[4 * j] / a.rho[kj];
@@ -747,7 +915,7 @@ hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     const size_t nthr = (size_t)pl.nseq * M * pl.P;
     hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_grad_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
-    hipLaunchKernelGGL((bwd_param_kernel<M>), dim3((unsigned)a.K_T), dim3(64), 0, s, a, pl);
+    hipLaunchKernelGGL((bwd_param_kernel<M>), dim3((unsigned)a.K_T), dim3(256), 0, s, a, pl);
     if (pl.nslice > 1) {
         const size_t total = (size_t)a.B * a.L * a.K_T;
         hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pl);

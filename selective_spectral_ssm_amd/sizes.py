@@ -19,6 +19,13 @@ workspace, re-reads or padding of an implementation:
               + P*s_io (v) + P*s_io (y) + 4 + 2*s_io (clock, gates)
               + 16*m (mode tables)
       flops = 10*m*P + 2*P
+
+  prefill backward, per (token, retained channel):
+      bytes = 3*P*s_io (v and dy read, dv written) + 4 + 2*s_io (clock, gates read)
+              + 3*4 (ddelta, dg_w, dg_r written, fp32)
+    plus, per call, the mode tables read (16 B per retained (k, j), 20 with zero-lag
+    coefficients) and their gradients written (same), and the entering state, the final
+    state's gradient and dstate_in (8 B each per retained (b, k, j, p)).
 """
 from __future__ import annotations
 
@@ -69,3 +76,14 @@ def decode_fused_flops(n_layers: int, B: int, K_T: int, m: int, P: int, d_model:
 
 def decode_flops(n_layers: int, B: int, K_T: int, m: int, P: int) -> int:
     return n_layers * B * K_T * (10 * m * P + 2 * P)
+
+
+def backward_bytes(B: int, L: int, K_T: int, m: int, P: int, io: str, zero_lag: bool = True,
+                   states: bool = True) -> int:
+    s = IO_BYTES[io]
+    per_tok = 3 * P * s + 4 + 2 * s + 12
+    tab = K_T * m * (20 if zero_lag else 16)
+    total = B * L * K_T * per_tok + 2 * tab
+    if states:
+        total += 3 * state_bytes(1, B, K_T, m, P)
+    return total

@@ -153,3 +153,42 @@ def test_backward_empty_sequence():
     assert essh.essh_mixer_prefill_backward(dims0, dummy, dummy, dummy, dummy, tab, tab, c, None, None, dummy,
                                             None, dummy, dummy, dummy, dummy, *outs, None) == essh.ESSH_OK
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Full workload sizes, in the launch configuration bench.py times: sampled channels against
+# the oracle run on those channels alone (channels are independent; the mode-table gradients
+# of a channel sum over every batch row, so every row of a sampled channel is kept).
+# ---------------------------------------------------------------------------
+
+FULL = [(1, (0, 23)), (2, (0, 31)), (4, (23,))]
+
+
+def _slice_channel(inp, k):
+    out = dict(io=inp["io"])
+    for key in ("v", "delta", "g_w", "g_r", "dy"):
+        out[key] = inp[key][:, :, k:k + 1]
+    for key in ("state_in", "dstate_out"):
+        out[key] = inp[key][:, k:k + 1]
+    for key in ("rho", "theta", "c", "zl"):
+        out[key] = inp[key][k:k + 1]
+    return out
+
+
+@pytest.mark.parametrize("widx,chans", FULL, ids=[f"workload{w}" for w, _ in FULL])
+def test_backward_full_size_sampled(widx, chans):
+    w = I.workload(widx)
+    K_T = w.K
+    log(f"full-size backward: {w.name} B={w.B} L={w.L} K_T={K_T} sampled channels {chans}")
+    inp = I.make_backward_inputs(w)
+    got = run_gpu_backward(inp, K_T)
+    for k in chans:
+        ref = oracle_grads(_slice_channel(inp, k), 1)
+        sub = {name: (np.take(got[name], [k], axis=CTRL_AXES[name]) if name in CTRL_AXES else got[name][k:k + 1])
+               for name in list(CTRL_AXES) + list(TABLES)}
+        errs = grad_errors(sub, ref, 1)
+        log(f"{w.name} channel {k}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        tol = TOL[inp["io"]]
+        for n, e in errs.items():
+            bar = tol if n == "dv" else F32_GRAD_TOL
+            assert e <= bar, f"{w.name} channel {k}: {n} error {e:.3e} > {bar:.0e}"
