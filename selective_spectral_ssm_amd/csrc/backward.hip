@@ -34,7 +34,8 @@
 //
 // Launches (one 64-lane wave per (sequence, segment, slice of <= 64 value columns)):
 //   1. bwd_agg_kernel   local state chain from zero over the segment (checkpoints after every
-//                       sub-block), local adjoint chain from zero, sub-block transfers;
+//                       sub-block) and sub-block transfers in one wave, the local adjoint chain
+//                       from zero in another;
 //   2. bwd_scan_kernel  scan over segments: entering states and arriving adjoints;
 //   3. bwd_grad_kernel  the sub-blocks of each segment in reverse, every gradient above;
 //   4. bwd_param_kernel sums the mode-table partials; with two slices bwd_combine_kernel adds
@@ -58,6 +59,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
+// the same with lanes whose source lies outside the row reading zero
+template <int CTRL>
+__device__ __forceinline__ float dpp_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;   // row_shr:n
 constexpr int DPP_XOR1 = 0xb1;          // quad_perm [1, 0, 3, 2]
 constexpr int DPP_XOR2 = 0x4e;          // quad_perm [2, 3, 0, 1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane l of each 8-lane half reads lane 7 - l
@@ -140,12 +147,12 @@ __device__ __forceinline__ SubCtl finish_ctl(const CtlRegs& r, int n, int i) {
     SubCtl c;
     c.gw = r.gw;
     c.gr = r.gr;
+    // inclusive prefix sum within the row of 16 lanes: DPP row shifts, zero from outside the row
     float q = r.dl;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        const float o = __shfl_up(q, off, 16);
-        if (i >= off) q += o;
-    }
+    q += dpp_zero<DPP_SHR1>(q);
+    q += dpp_zero<DPP_SHR2>(q);
+    q += dpp_zero<DPP_SHR4>(q);
+    q += dpp_zero<DPP_SHR8>(q);
     c.q = q;
     c.qe = __shfl(q, n - 1, 16);
     return c;
@@ -235,8 +242,9 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
     constexpr int NT = NTC / 16, ROWS = 2 * M, LD = NTC + 4;
     __shared__ Tables<M> T;
     __shared__ float tile[SB * LD];
+    __shared__ float apos[2][SB];   // q and one gate of each position of the sub-block
     const int lane = threadIdx.x, i = lane & 15, g = lane >> 4;
-    const int seg = blockIdx.x, sl = blockIdx.y, seq = blockIdx.z;
+    const int seg = blockIdx.x, sl = blockIdx.y >> 1, adjoint = blockIdx.y & 1, seq = blockIdx.z;
     const int k = seq % a.K_T, b = seq / a.K_T;
     const int s0 = seg * pl.Ls, len = min(pl.Ls, a.L - s0), nsb = (len + SB - 1) / SB;
     const int col0 = sl * NTC;
@@ -246,38 +254,40 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
     const IO* dsrc = static_cast<const IO*>(a.dy) + (((size_t)b * a.L) * a.K + k) * pl.P + col0;
     auto sub_n = [&](int sb) { return min(SB, s0 + len - (s0 + sb * SB)); };
     build_tables<M>(T, a, k, lane);
-
+    CtlRegs cr;
+    TileRegs<IO, NTC> tv;
+    if (!adjoint) {   // the two chains run in separate waves
     // local state chain from zero; checkpoint after every sub-block
     f32x4 st[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float2 tr0 = make_float2(1.f, 0.f), tr1 = make_float2(1.f, 0.f);
-    CtlRegs cr = load_ctl_regs<IO>(a, b, k, s0, sub_n(0), i);
-    TileRegs<IO, NTC> tv;
+    cr = load_ctl_regs<IO>(a, b, k, s0, sub_n(0), i);
     tv.load(vsrc + (size_t)s0 * rs, rs, sub_n(0), lane);
     for (int sb = 0; sb < nsb; ++sb) {
         const int n = sub_n(sb);
         const SubCtl c = finish_ctl(cr, n, i);
         tv.template store<LD>(tile, lane);
+        if (g == 0) {
+            apos[0][i] = c.q;
+            apos[1][i] = c.gw;
+        }
         if (sb + 1 < nsb) {
             const int t1 = s0 + (sb + 1) * SB;
             cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb + 1), i);
             tv.load(vsrc + (size_t)t1 * rs, rs, sub_n(sb + 1), lane);
         }
+        const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
+        __syncthreads();
         float wa[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int s = 4 * kk + g;
-            const float qs = __shfl(c.q, s, 16), gws = __shfl(c.gw, s, 16);
-            float w = 0.f;
-            if (i < ROWS && s < n) {
-                const float2 p = T.pw[n - 1 - s][i >> 1];
-                w = ((i & 1) ? p.y : p.x) * expf(qs - c.qe) * gws;
-            }
-            wa[kk] = w;
+            const bool ok = i < ROWS && s < n;
+            const float2 p = T.pw[ok ? n - 1 - s : 0][i < ROWS ? i >> 1 : 0];
+            const float w = ((i & 1) ? p.y : p.x) * expf(apos[0][s] - c.qe) * apos[1][s];
+            wa[kk] = ok ? w : 0.f;
         }
-        const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
-        __syncthreads();
         float* ck = pl.ck + ((segi * pl.nsb + sb) * ROWS) * (size_t)pl.P + col0;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -306,7 +316,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         if (2 * g < M) pl.lam[segi * M + 2 * g] = tr0;
         if (2 * g + 1 < M) pl.lam[segi * M + 2 * g + 1] = tr1;
     }
-
+    } else {
     // local adjoint chain from zero, last sub-block first
     f32x4 bt[NT];
 #pragma unroll
@@ -320,25 +330,26 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         const int n = sub_n(sb);
         const SubCtl c = finish_ctl(cr, n, i);
         tv.template store<LD>(tile, lane);
+        if (g == 0) {
+            apos[0][i] = c.q;
+            apos[1][i] = c.gr;
+        }
         if (sb > 0) {
             const int t1 = s0 + (sb - 1) * SB;
             cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb - 1), i);
             tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(sb - 1), lane);
         }
+        const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
+        __syncthreads();
         float ca[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int u = 4 * kk + g;
-            const float qu = __shfl(c.q, u, 16), gru = __shfl(c.gr, u, 16);
-            float w = 0.f;
-            if (i < ROWS && u < n) {
-                const float2 cp = T.cpw[u + 1][i >> 1];
-                w = gru * expf(-qu) * ((i & 1) ? -cp.y : cp.x);
-            }
-            ca[kk] = w;
+            const bool ok = i < ROWS && u < n;
+            const float2 cp = T.cpw[u + 1][i < ROWS ? i >> 1 : 0];
+            const float w = apos[1][u] * expf(-apos[0][u]) * ((i & 1) ? -cp.y : cp.x);
+            ca[kk] = ok ? w : 0.f;
         }
-        const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
-        __syncthreads();
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 d;   // conj(transfer) applied to the adjoint
@@ -358,6 +369,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (4 * g + r < ROWS) sa[(size_t)(4 * g + r) * pl.P + nt * 16 + i] = bt[nt][r];
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -911,7 +923,8 @@ __global__ void __launch_bounds__(256) bwd_combine_kernel(BackwardArgs a, BwdPla
 template <int M, int NTC, typename IO>
 hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     const dim3 grid((unsigned)pl.nseg, (unsigned)pl.nslice, (unsigned)pl.nseq);
-    hipLaunchKernelGGL((bwd_agg_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
+    const dim3 grid2((unsigned)pl.nseg, (unsigned)(2 * pl.nslice), (unsigned)pl.nseq);   // state and adjoint chains
+    hipLaunchKernelGGL((bwd_agg_kernel<M, NTC, IO>), grid2, dim3(64), 0, s, a, pl);
     const size_t nthr = (size_t)pl.nseq * M * pl.P;
     hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_grad_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
@@ -947,22 +960,31 @@ hipError_t launch_io(const BackwardArgs& a, int m, const BwdPlan& pl, hipStream_
 
 }  // namespace
 
+// Resident waves of the gradient kernel on the whole GPU (256 CUs x 4 SIMDs x its occupancy:
+// two waves per SIMD, one for m = 8 with 64-column slices).
+static int grad_wave_slots(int m, int P) { return (m == 8 && P >= 64) ? 1024 : 2048; }
+
 BwdPlan plan_backward(int B, int L, int K, int K_T, int m, int P) {
     BwdPlan pl{};
     pl.P = P;
     pl.nslice = P > 64 ? P / 64 : 1;
     pl.nseq = B * K_T;
-    // enough waves to fill the GPU: about 2048 (sequence, segment, slice) triples
+    pl.nctl = (size_t)B * L * K;
+    // segments per sequence: the waves (sequence, segment, slice) fill whole rounds of the
+    // gradient kernel's resident slots, with segments of at most MAX_BWD_SUBBLOCKS sub-blocks
     const long long per = (long long)pl.nseq * pl.nslice;
-    long long nseg = per > 0 ? (2048 + per - 1) / per : 1;
-    if (nseg < 1) nseg = 1;
-    long long ls = L > 0 ? ((L + nseg - 1) / nseg + SB - 1) / SB * SB : SB;
-    if (ls < SB) ls = SB;
-    if (ls > MAX_BWD_SUBBLOCKS * SB) ls = MAX_BWD_SUBBLOCKS * SB;
+    const long long slots = grad_wave_slots(m, P);
+    long long ls = SB;
+    for (long long r = 1;; ++r) {
+        long long nseg = per > 0 ? (slots * r) / per : 1;
+        if (nseg < 1) nseg = 1;
+        ls = L > 0 ? ((L + nseg - 1) / nseg + SB - 1) / SB * SB : SB;
+        if (ls < SB) ls = SB;
+        if (ls <= (long long)MAX_BWD_SUBBLOCKS * SB) break;
+    }
     pl.Ls = (int)ls;
     pl.nseg = L > 0 ? (int)((L + ls - 1) / ls) : 1;
     pl.nsb = (int)(ls / SB);
-    pl.nctl = (size_t)B * L * K;
     return pl;
 }
 

@@ -124,7 +124,7 @@ struct BackwardArgs {
 //   lam  [nseq][nseg][m]           segment transfers (complex)
 //   pp   [nseq][nseg][nslice][4m+1] mode-table partials (Omega_j, Gamma_j, trace)
 //   part [nslice][B L K][3]        per-slice ddelta, dg_w, dg_r (nslice > 1 only)
-constexpr int MAX_BWD_SUBBLOCKS = 64;
+constexpr int MAX_BWD_SUBBLOCKS = 128;
 struct BwdPlan {
     int P, nslice, nseq, nseg, Ls, nsb;
     size_t nctl;              // B L K
