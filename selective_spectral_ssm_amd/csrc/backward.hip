@@ -38,8 +38,9 @@
 //                       from zero in another;
 //   2. bwd_scan_kernel  scan over segments: entering states and arriving adjoints;
 //   3. bwd_grad_kernel  the sub-blocks of each segment in reverse, every gradient above;
-//   4. bwd_param_kernel sums the mode-table partials; with two slices bwd_combine_kernel adds
-//                       the per-position partials.
+//   4. bwd_param_kernel sums the mode-table partials;
+// around them bwd_pack_kernel makes a channel-major copy of the controls and bwd_unpack_kernel
+// turns the channel-major control gradients (summed over column slices) back into [B, L, K].
 // MFMA layouts (16x16x4 f32): A operand lane l = A[l % 16][l / 16], B operand lane l =
 // B[l / 16][l % 16], result lane l register r = D[4 (l / 16) + r][l % 16].  A state [2m rows]
 // [columns] is held as 16-column result tiles (rows 4g..4g+3 of column i in lane (g, i)).
@@ -128,18 +129,15 @@ struct SubCtl {
     float gw, gr, q, qe;
 };
 
-template <typename IO>
-__device__ __forceinline__ CtlRegs load_ctl_regs(const BackwardArgs& a, int b, int k, int t0, int n, int i) {
-    using io = io_traits<IO>;
+// from the channel-major copy of the controls (one 16-byte load per position)
+__device__ __forceinline__ CtlRegs load_ctl_regs(const BackwardArgs& a, const BwdPlan& pl, int seq, int t0, int n,
+                                                 int i) {
     CtlRegs c;
     const bool in = i < n;
-    const size_t row = ((size_t)b * a.L + t0 + (in ? i : 0)) * a.K + k;   // clamped: always a valid address
-    const float dl = a.delta[row];
-    const float gw = io::load(static_cast<const IO*>(a.g_w), row);
-    const float gr = io::load(static_cast<const IO*>(a.g_r), row);
-    c.dl = in ? dl : 0.f;
-    c.gw = in ? gw : 0.f;
-    c.gr = in ? gr : 0.f;
+    const float4 x = pl.pc[(size_t)seq * a.L + t0 + (in ? i : 0)];   // clamped: always a valid address
+    c.dl = in ? x.x : 0.f;
+    c.gw = in ? x.y : 0.f;
+    c.gr = in ? x.z : 0.f;
     return c;
 }
 
@@ -235,6 +233,73 @@ __device__ __forceinline__ float2 sub_transfer(const Tables<M>& T, int j, int n,
 }
 
 // ------------------------------------------------------------------------------------------
+// 0. channel-major copy of the controls: pc[seq][t] = (delta, g_w, g_r, 0), seq = b K_T + k.
+//    One workgroup per 64 positions x 32 channels of one batch row, transposed through LDS so
+//    that the reads (along the channels of a position) and the writes (along the positions of
+//    a channel) are contiguous.  bwd_unpack_kernel is its reverse for the control gradients.
+// ------------------------------------------------------------------------------------------
+constexpr int PK_T = 64, PK_K = 32;
+
+template <typename IO>
+__global__ void __launch_bounds__(256) bwd_pack_kernel(BackwardArgs a, BwdPlan pl) {
+    __shared__ float sd[3][PK_K][PK_T + 1];
+    using io = io_traits<IO>;
+    const int t0 = blockIdx.x * PK_T, k0 = blockIdx.y * PK_K, b = blockIdx.z;
+    for (int idx = threadIdx.x; idx < PK_K * PK_T; idx += 256) {
+        const int pos = idx / PK_K, kk = idx % PK_K;
+        const int t = t0 + pos, k = k0 + kk;
+        if (t < a.L && k < a.K_T) {
+            const size_t row = ((size_t)b * a.L + t) * a.K + k;
+            sd[0][kk][pos] = a.delta[row];
+            sd[1][kk][pos] = io::load(static_cast<const IO*>(a.g_w), row);
+            sd[2][kk][pos] = io::load(static_cast<const IO*>(a.g_r), row);
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < PK_K * PK_T; idx += 256) {
+        const int kk = idx / PK_T, pos = idx % PK_T;
+        const int t = t0 + pos, k = k0 + kk;
+        if (t < a.L && k < a.K_T)
+            pl.pc[((size_t)b * a.K_T + k) * a.L + t] = make_float4(sd[0][kk][pos], sd[1][kk][pos], sd[2][kk][pos], 0.f);
+    }
+}
+
+// control gradients from the channel-major (ddelta, dg_w, dg_r) of every column slice, summed
+// over the slices, into the [B, L, K] outputs
+__global__ void __launch_bounds__(256) bwd_unpack_kernel(BackwardArgs a, BwdPlan pl) {
+    __shared__ float sd[3][PK_K][PK_T + 1];
+    const int t0 = blockIdx.x * PK_T, k0 = blockIdx.y * PK_K, b = blockIdx.z;
+    for (int idx = threadIdx.x; idx < PK_K * PK_T; idx += 256) {
+        const int kk = idx / PK_T, pos = idx % PK_T;
+        const int t = t0 + pos, k = k0 + kk;
+        if (t < a.L && k < a.K_T) {
+            const size_t o = ((size_t)b * a.K_T + k) * a.L + t;
+            float4 x = pl.gc[o];
+            for (int sl = 1; sl < pl.nslice; ++sl) {
+                const float4 y = pl.gc[(size_t)sl * pl.nseq * a.L + o];
+                x.x += y.x;
+                x.y += y.y;
+                x.z += y.z;
+            }
+            sd[0][kk][pos] = x.x;
+            sd[1][kk][pos] = x.y;
+            sd[2][kk][pos] = x.z;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < PK_K * PK_T; idx += 256) {
+        const int pos = idx / PK_K, kk = idx % PK_K;
+        const int t = t0 + pos, k = k0 + kk;
+        if (t < a.L && k < a.K_T) {
+            const size_t row = ((size_t)b * a.L + t) * a.K + k;
+            a.ddelta[row] = sd[0][kk][pos];
+            a.dg_w[row] = sd[1][kk][pos];
+            a.dg_r[row] = sd[2][kk][pos];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // 1. segment aggregates
 // ------------------------------------------------------------------------------------------
 template <int M, int NTC, typename IO>
@@ -262,7 +327,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float2 tr0 = make_float2(1.f, 0.f), tr1 = make_float2(1.f, 0.f);
-    cr = load_ctl_regs<IO>(a, b, k, s0, sub_n(0), i);
+    cr = load_ctl_regs(a, pl, seq, s0, sub_n(0), i);
     tv.load(vsrc + (size_t)s0 * rs, rs, sub_n(0), lane);
     for (int sb = 0; sb < nsb; ++sb) {
         const int n = sub_n(sb);
@@ -274,7 +339,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         }
         if (sb + 1 < nsb) {
             const int t1 = s0 + (sb + 1) * SB;
-            cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb + 1), i);
+            cr = load_ctl_regs(a, pl, seq, t1, sub_n(sb + 1), i);
             tv.load(vsrc + (size_t)t1 * rs, rs, sub_n(sb + 1), lane);
         }
         const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
@@ -323,7 +388,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
     for (int nt = 0; nt < NT; ++nt) bt[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
         const int t1 = s0 + (nsb - 1) * SB;
-        cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(nsb - 1), i);
+        cr = load_ctl_regs(a, pl, seq, t1, sub_n(nsb - 1), i);
         tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(nsb - 1), lane);
     }
     for (int sb = nsb - 1; sb >= 0; --sb) {
@@ -336,7 +401,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         }
         if (sb > 0) {
             const int t1 = s0 + (sb - 1) * SB;
-            cr = load_ctl_regs<IO>(a, b, k, t1, sub_n(sb - 1), i);
+            cr = load_ctl_regs(a, pl, seq, t1, sub_n(sb - 1), i);
             tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(sb - 1), lane);
         }
         const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
@@ -492,7 +557,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
     const int col0 = sl * NTC, P = pl.P;
     const size_t rs = (size_t)a.K * P;
     const size_t segi = (size_t)seq * pl.nseg + seg;
-    const size_t rowb = ((size_t)b * a.L) * a.K + k;      // control index of position 0
+    const size_t rowb = ((size_t)b * a.L) * a.K + k;      // row (b, position 0, k) of the [B, L, K] arrays
     const IO* vsrc = static_cast<const IO*>(a.v) + rowb * P + col0;
     const IO* dsrc = static_cast<const IO*>(a.dy) + rowb * P + col0;
     auto sub_n = [&](int sb) { return min(SB, s0 + len - (s0 + sb * SB)); };
@@ -570,7 +635,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
     {
         const int t1 = s0 + (nsb - 1) * SB, n1 = sub_n(nsb - 1);
         load_ck(ckn, nsb - 1);
-        crn = load_ctl_regs<IO>(a, b, k, t1, n1, i);
+        crn = load_ctl_regs(a, pl, seq, t1, n1, i);
         tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
         tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
     }
@@ -597,7 +662,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
         if (sb > 0) {   // inputs of the next sub-block (the one before) go out now
             const int t1 = t0 - SB, n1 = sub_n(sb - 1);
             load_ck(ckn, sb - 1);
-            crn = load_ctl_regs<IO>(a, b, k, t1, n1, i);
+            crn = load_ctl_regs(a, pl, seq, t1, n1, i);
             tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
             tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
         }
@@ -731,19 +796,8 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
                 if (i + off < 16) cs += o;
             }
             const float ddl = cs - xe;
-            if (g == 0 && i < n) {
-                const size_t ci = rowb + (size_t)(t0 + i) * a.K;
-                if (pl.nslice == 1) {
-                    a.ddelta[ci] = ddl;
-                    a.dg_w[ci] = dgw;
-                    a.dg_r[ci] = dgr;
-                } else {
-                    float* part = pl.part + ((size_t)sl * pl.nctl + ci) * 3;
-                    part[0] = ddl;
-                    part[1] = dgw;
-                    part[2] = dgr;
-                }
-            }
+            if (g == 0 && i < n)
+                pl.gc[((size_t)sl * pl.nseq + seq) * a.L + t0 + i] = make_float4(ddl, dgw, dgr, 0.f);
         }
 
         // ---- dv = g_w (G^T dY + W^T B1), staged in the v tile ----
@@ -906,22 +960,10 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(BackwardArgs a, BwdPlan 
     }
 }
 
-__global__ void __launch_bounds__(256) bwd_combine_kernel(BackwardArgs a, BwdPlan pl) {
-    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)a.B * a.L * a.K_T;
-    if (tid >= total) return;
-    const int k = (int)(tid % a.K_T);
-    const size_t bt = tid / a.K_T;
-    const size_t ci = bt * a.K + k;
-    const float* p0 = pl.part + ci * 3;
-    const float* p1 = pl.part + (pl.nctl + ci) * 3;
-    a.ddelta[ci] = p0[0] + p1[0];
-    a.dg_w[ci] = p0[1] + p1[1];
-    a.dg_r[ci] = p0[2] + p1[2];
-}
-
 template <int M, int NTC, typename IO>
 hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
+    const dim3 pgrid((unsigned)((a.L + PK_T - 1) / PK_T), (unsigned)((a.K_T + PK_K - 1) / PK_K), (unsigned)a.B);
+    hipLaunchKernelGGL((bwd_pack_kernel<IO>), pgrid, dim3(256), 0, s, a, pl);
     const dim3 grid((unsigned)pl.nseg, (unsigned)pl.nslice, (unsigned)pl.nseq);
     const dim3 grid2((unsigned)pl.nseg, (unsigned)(2 * pl.nslice), (unsigned)pl.nseq);   // state and adjoint chains
     hipLaunchKernelGGL((bwd_agg_kernel<M, NTC, IO>), grid2, dim3(64), 0, s, a, pl);
@@ -929,10 +971,7 @@ hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_grad_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_param_kernel<M>), dim3((unsigned)a.K_T), dim3(256), 0, s, a, pl);
-    if (pl.nslice > 1) {
-        const size_t total = (size_t)a.B * a.L * a.K_T;
-        hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, pl);
-    }
+    hipLaunchKernelGGL(bwd_unpack_kernel, pgrid, dim3(256), 0, s, a, pl);
     return hipGetLastError();
 }
 
@@ -969,7 +1008,7 @@ BwdPlan plan_backward(int B, int L, int K, int K_T, int m, int P) {
     pl.P = P;
     pl.nslice = P > 64 ? P / 64 : 1;
     pl.nseq = B * K_T;
-    pl.nctl = (size_t)B * L * K;
+    pl.L = L;
     // segments per sequence: the waves (sequence, segment, slice) fill whole rounds of the
     // gradient kernel's resident slots, with segments of at most MAX_BWD_SUBBLOCKS sub-blocks
     const long long per = (long long)pl.nseq * pl.nslice;
@@ -1000,7 +1039,8 @@ size_t backward_workspace_bytes(int B, int L, int K, int K_T, int m, int P) {
     add(segs * pl.nsb * m * 2);          // ltr
     add(segs * m * 2);                   // lam
     add(segs * pl.nslice * (4 * m + 1)); // pp
-    if (pl.nslice > 1) add(pl.nslice * pl.nctl * 3);   // part
+    add((size_t)pl.nseq * L * 4);        // pc
+    add((size_t)pl.nslice * pl.nseq * L * 4);   // gc
     return bytes;
 }
 
@@ -1019,7 +1059,8 @@ void bind_backward_workspace(BwdPlan& pl, void* ws, int m) {
     pl.ltr = reinterpret_cast<float2*>(take(segs * pl.nsb * m * 2));
     pl.lam = reinterpret_cast<float2*>(take(segs * m * 2));
     pl.pp = take(segs * pl.nslice * (4 * m + 1));
-    pl.part = pl.nslice > 1 ? take(pl.nslice * pl.nctl * 3) : nullptr;
+    pl.pc = reinterpret_cast<float4*>(take((size_t)pl.nseq * pl.L * 4));
+    pl.gc = reinterpret_cast<float4*>(take((size_t)pl.nslice * pl.nseq * pl.L * 4));
 }
 
 hipError_t launch_prefill_backward(const BackwardArgs& a, int m, const BwdPlan& pl, int io_dtype, hipStream_t s) {

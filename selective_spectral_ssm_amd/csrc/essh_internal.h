@@ -123,18 +123,19 @@ struct BackwardArgs {
 //   ltr  [nseq][nseg][nsb][m]      sub-block transfers lambda_j^n e^{-q(n-1)} (complex)
 //   lam  [nseq][nseg][m]           segment transfers (complex)
 //   pp   [nseq][nseg][nslice][4m+1] mode-table partials (Omega_j, Gamma_j, trace)
-//   part [nslice][B L K][3]        per-slice ddelta, dg_w, dg_r (nslice > 1 only)
+//   pc   [nseq][L]                 channel-major controls (delta, g_w, g_r, 0)
+//   gc   [nslice][nseq][L]         channel-major control gradients (ddelta, dg_w, dg_r, 0)
 constexpr int MAX_BWD_SUBBLOCKS = 128;
 struct BwdPlan {
-    int P, nslice, nseq, nseg, Ls, nsb;
-    size_t nctl;              // B L K
+    int P, nslice, nseq, nseg, Ls, nsb, L;
     float* ck;
     float* sa;
     float* hin;
     float2* ltr;
     float2* lam;
     float* pp;
-    float* part;
+    float4* pc;
+    float4* gc;
 };
 
 // Work split of the chunked prefill.  nseq = B * K_T sequences of nchunks
