@@ -32,7 +32,7 @@
 // N depends on the sub-block only through (u, s), so it is summed over all sub-blocks first
 // and weighted once at the end; the parts through H0 and B1 are summed the same way.
 //
-// Launches (one 64-lane wave per (sequence, segment, slice of <= 64 value columns)):
+// Launches (one 64-lane wave per (sequence, segment, slice of 64 value columns, 32 with m = 8)):
 //   1. bwd_agg_kernel   local state chain from zero over the segment (checkpoints after every
 //                       sub-block) and sub-block transfers in one wave, the local adjoint chain
 //                       from zero in another;
@@ -55,12 +55,8 @@ constexpr int SB = 16;            // positions per sub-block
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// DPP lane moves within a row of 16 lanes (row_mask and bank_mask all on)
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-// the same with lanes whose source lies outside the row reading zero
+// DPP lane move within a row of 16 lanes (row_mask and bank_mask all on); lanes whose source
+// lies outside the row read zero
 template <int CTRL>
 __device__ __forceinline__ float dpp_zero(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
@@ -71,12 +67,14 @@ constexpr int DPP_XOR2 = 0x4e;          // quad_perm [2, 3, 0, 1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane l of each 8-lane half reads lane 7 - l
 constexpr int DPP_MIRROR = 0x140;       // lane l of each row reads lane 15 - l
 
-// sum over the 16 lanes of one row group (equal lane >> 4); every lane gets the total
+// sum over the 16 lanes of one row group (equal lane >> 4); every lane gets the total (every
+// source lane lies inside the row, so the zero-fill form is exact and lets the move fold into
+// the add)
 __device__ __forceinline__ float row_sum16(float x) {
-    x += dpp<DPP_XOR1>(x);
-    x += dpp<DPP_XOR2>(x);
-    x += dpp<DPP_HALF_MIRROR>(x);
-    x += dpp<DPP_MIRROR>(x);
+    x += dpp_zero<DPP_XOR1>(x);
+    x += dpp_zero<DPP_XOR2>(x);
+    x += dpp_zero<DPP_HALF_MIRROR>(x);
+    x += dpp_zero<DPP_MIRROR>(x);
     return x;
 }
 // sum over the four row groups (equal lane & 15)
@@ -368,10 +366,10 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             for (int r = 0; r < 4; ++r)
                 if (4 * g + r < ROWS) ck[(size_t)(4 * g + r) * pl.P + nt * 16 + i] = d[r];
         }
-        if (sl == 0 && i == 0) {
-            float2* ltr = pl.ltr + (segi * pl.nsb + sb) * M;
-            if (2 * g < M) ltr[2 * g] = l0;
-            if (2 * g + 1 < M) ltr[2 * g + 1] = l1;
+        if (sl == 0 && i == 0) {   // transfer from the segment start to this sub-block's start
+            float2* tpf = pl.tpf + (segi * pl.nsb + sb) * M;
+            if (2 * g < M) tpf[2 * g] = tr0;
+            if (2 * g + 1 < M) tpf[2 * g + 1] = tr1;
         }
         tr0 = cmul(l0, tr0);
         tr1 = cmul(l1, tr1);
@@ -535,15 +533,16 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan p
 // 3. gradients of every sub-block
 // ------------------------------------------------------------------------------------------
 template <int M, int NTC, typename IO>
-__global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan pl) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bwd_grad_kernel(BackwardArgs a,
+                                                                                          BwdPlan pl) {
     constexpr int NT = NTC / 16, ROWS = 2 * M, KR = (ROWS + 3) / 4, LD = NTC + 4, KS = NTC / 4, LM = SB + 1;
     constexpr int CKN = M * NTC, CKE = (CKN + 63) / 64;   // complex state entries, per lane
     __shared__ Tables<M> T;
     __shared__ float vt[SB * LD], dyt[SB * LD];   // v tile (then the dv tile) and dy tile
-    __shared__ float hbuf[2][SB * LD];            // states entering the sub-block and leaving it
-    __shared__ float hin[ROWS * LD];              // the segment's entering state
-    __shared__ float b1m[SB * LD];                // adjoint arriving at the sub-block's end
-    __shared__ float2 tpref[MAX_BWD_SUBBLOCKS + 1][M];
+    // state entering the sub-block and adjoint arriving at its end, [row][column]; row 2m stays
+    // zero and stands in for every row >= 2m that an operand read asks for
+    __shared__ float hs[(ROWS + 1) * LD];
+    __shared__ float b1m[(ROWS + 1) * LD];
     __shared__ float pos[5][SB];                  // q, g_r, g_w, e^{-q}, e^{-(q(n-1) - q)}
     __shared__ float GT[SB * LM];                 // [s][u] = g_r(u) e^{-(q(u)-q(s))} psi(u - s), u >= s
     __shared__ float WQ[SB * LM];                 // [u][row] = e^{-q(u)} {Re, -Im}(c_j lambda_j^{u+1})
@@ -563,25 +562,21 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
     auto sub_n = [&](int sb) { return min(SB, s0 + len - (s0 + sb * SB)); };
     build_tables<M>(T, a, k, lane);
 
-    for (int idx = lane; idx < ROWS * NTC; idx += 64) {
-        const int r = idx / NTC, col = idx - r * NTC;
-        hin[r * LD + col] = pl.hin[(segi * ROWS + r) * (size_t)P + col0 + col];
-    }
-    // rows 2m..15 of the state and adjoint buffers stay zero, so that they can be read as
-    // operands without a bound check
-    for (int idx = ROWS * LD + lane; idx < SB * LD; idx += 64) {
-        hbuf[0][idx] = 0.f;
-        hbuf[1][idx] = 0.f;
+    for (int idx = lane; idx < (ROWS + 1) * LD; idx += 64) {
+        hs[idx] = 0.f;
         b1m[idx] = 0.f;
     }
-    if (lane < M) {   // transfer from the segment start to the start of every sub-block
-        float2 t = make_float2(1.f, 0.f);
-        tpref[0][lane] = t;
-        for (int sb = 0; sb < nsb; ++sb) {
-            t = cmul(pl.ltr[(segi * pl.nsb + sb) * M + lane], t);
-            tpref[sb + 1][lane] = t;
-        }
+    // the segment's entering state at this lane's (mode, column) entries
+    float2 hinr[CKE];
+#pragma unroll
+    for (int e = 0; e < CKE; ++e) {
+        const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
+        const bool ok = CKN % 64 == 0 || idx < CKN;
+        const float* h = pl.hin + (segi * ROWS + 2 * (ok ? j : 0)) * (size_t)P + col0 + (ok ? col : 0);
+        const float xr = h[0], xi = h[P];
+        hinr[e] = ok ? make_float2(xr, xi) : make_float2(0.f, 0.f);
     }
+    __syncthreads();
     f32x4 b1[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -590,7 +585,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
             const int row = 4 * g + r;
             const float x = row < ROWS ? pl.sa[(segi * ROWS + row) * (size_t)P + col0 + nt * 16 + i] : 0.f;
             b1[nt][r] = x;
-            b1m[row * LD + nt * 16 + i] = x;
+            if (row < ROWS) b1m[row * LD + nt * 16 + i] = x;
         }
 
     // local checkpoint after sub-block sb - 1 (zero for sb = 0), at this lane's entries
@@ -605,36 +600,57 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
             ckr[e] = ok ? make_float2(xr, xi) : make_float2(0.f, 0.f);
         }
     };
+    // transfer from the segment start to the start of sub-block sb (sb = nsb: the segment end)
+    auto load_tp = [&](float2 (&tpr)[CKE], int sb) {
+#pragma unroll
+        for (int e = 0; e < CKE; ++e) {
+            const int idx = lane + 64 * e, j = (CKN % 64 == 0 || idx < CKN) ? idx / NTC : 0;
+            tpr[e] = sb < nsb ? pl.tpf[(segi * pl.nsb + sb) * M + j] : pl.lam[segi * M + j];
+        }
+    };
     // true state entering sub-block sb: the checkpoint plus the segment's entering state
     // carried by the transfer from the segment start
-    auto put_state = [&](float* hs, const float2 (&ckr)[CKE], int sb) {
+    auto put_state = [&](const float2 (&ckr)[CKE], const float2 (&tpr)[CKE]) {
 #pragma unroll
         for (int e = 0; e < CKE; ++e) {
             const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
             if (CKN % 64 == 0 || idx < CKN) {
-                const float2 t = tpref[sb][j];
-                const float hr = hin[2 * j * LD + col], hi = hin[(2 * j + 1) * LD + col];
-                hs[2 * j * LD + col] = ckr[e].x + t.x * hr - t.y * hi;
-                hs[(2 * j + 1) * LD + col] = ckr[e].y + t.x * hi + t.y * hr;
+                const float2 t = tpr[e], h = hinr[e];
+                hs[2 * j * LD + col] = ckr[e].x + t.x * h.x - t.y * h.y;
+                hs[(2 * j + 1) * LD + col] = ckr[e].y + t.x * h.y + t.y * h.x;
             }
         }
     };
-    // a state's entry of result-layout register r of tile nt (rows >= 2m read as zero)
-    auto st_at = [&](const float* hs, int nt, int r) { return hs[(4 * g + r) * LD + nt * 16 + i]; };
+    // entry of a [row][column] LDS state at result-layout register r of tile nt (rows >= 2m: the
+    // zero row)
+    auto st_at = [&](const float* h, int nt, int r) { return h[min(4 * g + r, ROWS) * LD + nt * 16 + i]; };
+    // Re sum_j conj(B1_j) . h_j over this slice's columns (h in hs)
+    auto inner_b1 = [&](const f32x4 (&bb)[NT]) {
+        float x = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x += bb[nt][r] * st_at(hs, nt, r);
+        return wave_sum64(x);
+    };
 
-    __syncthreads();
-    int cur = 0;   // hbuf[cur]: state leaving the sub-block being processed
+    // inner product of the arriving adjoint with the state leaving the last sub-block
+    float xe;
     {
-        float2 ckr[CKE];
+        float2 ckr[CKE], tpr[CKE];
         load_ck(ckr, nsb);
-        put_state(hbuf[cur], ckr, nsb);
+        load_tp(tpr, nsb);
+        put_state(ckr, tpr);
+        __syncthreads();
+        xe = inner_b1(b1);
     }
-    float2 ckn[CKE];
+    float2 ckn[CKE], tpn[CKE];
     CtlRegs crn;
     TileRegs<IO, NTC> tvn, tdn;
     {
         const int t1 = s0 + (nsb - 1) * SB, n1 = sub_n(nsb - 1);
         load_ck(ckn, nsb - 1);
+        load_tp(tpn, nsb - 1);
         crn = load_ctl_regs(a, pl, seq, t1, n1, i);
         tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
         tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
@@ -649,9 +665,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
         const SubCtl c = finish_ctl(crn, n, i);
         tvn.template store<LD>(vt, lane);
         tdn.template store<LD>(dyt, lane);
-        float* hs = hbuf[cur ^ 1];     // state entering this sub-block
-        const float* hn = hbuf[cur];   // state leaving it
-        put_state(hs, ckn, sb);
+        put_state(ckn, tpn);
         if (g == 0) {
             pos[0][i] = c.q;
             pos[1][i] = c.gr;
@@ -662,6 +676,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
         if (sb > 0) {   // inputs of the next sub-block (the one before) go out now
             const int t1 = t0 - SB, n1 = sub_n(sb - 1);
             load_ck(ckn, sb - 1);
+            load_tp(tpn, sb - 1);
             crn = load_ctl_regs(a, pl, seq, t1, n1, i);
             tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
             tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
@@ -691,15 +706,16 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
         f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f}, Q = S, R = S;
         {
             const int ir = i < n ? n - 1 - i : SB - 1;   // reversed row of V for R (row 15 is zero when n < 16)
+            const int ri = min(i, ROWS);                 // state row i (rows >= 2m: the zero row)
             // four columns per 16-byte LDS read; one group at a time keeps few operands live
 #pragma unroll 1
             for (int k4 = 0; k4 < KS; k4 += 4) {
                 const int col = g * KS + k4;
                 const float4 d4 = *reinterpret_cast<const float4*>(dyt + i * LD + col);
                 const float4 v4 = *reinterpret_cast<const float4*>(vt + i * LD + col);
-                const float4 h4 = *reinterpret_cast<const float4*>(hs + i * LD + col);
+                const float4 h4 = *reinterpret_cast<const float4*>(hs + ri * LD + col);
                 const float4 r4 = *reinterpret_cast<const float4*>(vt + ir * LD + col);
-                const float4 b4 = *reinterpret_cast<const float4*>(b1m + i * LD + col);
+                const float4 b4 = *reinterpret_cast<const float4*>(b1m + ri * LD + col);
                 S = mfma4(d4.x, v4.x, S);
                 Q = mfma4(d4.x, h4.x, Q);
                 R = mfma4(r4.x, b4.x, R);
@@ -754,22 +770,19 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
             if (s >= 0) red[3][s] = esel;
         }
 
-        // ---- inner products of the arriving adjoint with the end and entering states ----
-        float xe = 0.f, z0r = 0.f, z0i = 0.f, z1r = 0.f, z1i = 0.f;
+        // ---- inner products of the arriving adjoint with the entering state (per mode); the
+        //      one with the leaving state (xe) was formed with the sub-block after ----
+        float z0r = 0.f, z0i = 0.f, z1r = 0.f, z1i = 0.f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             float h0[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                xe += b1[nt][r] * st_at(hn, nt, r);
-                h0[r] = st_at(hs, nt, r);
-            }
+            for (int r = 0; r < 4; ++r) h0[r] = st_at(hs, nt, r);
             z0r += b1[nt][0] * h0[0] + b1[nt][1] * h0[1];
             z0i += b1[nt][0] * h0[1] - b1[nt][1] * h0[0];
             z1r += b1[nt][2] * h0[2] + b1[nt][3] * h0[3];
             z1i += b1[nt][2] * h0[3] - b1[nt][3] * h0[2];
         }
-        xe = wave_sum64(xe);
         z0r = row_sum16(z0r);
         z0i = row_sum16(z0i);
         z1r = row_sum16(z1r);
@@ -814,9 +827,7 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) d = mfma4(ga[kk], dyt[(4 * kk + g) * LD + col], d);
 #pragma unroll
-                for (int kk = 0; kk < KR; ++kk) {
-                    d = mfma4(wt[kk], b1m[(4 * kk + g) * LD + col], d);
-                }
+                for (int kk = 0; kk < KR; ++kk) d = mfma4(wt[kk], b1m[min(4 * kk + g, ROWS) * LD + col], d);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vt[(4 * g + r) * LD + col] = pos[2][4 * g + r] * d[r];
             }
@@ -842,13 +853,14 @@ __global__ void __launch_bounds__(64, 2) bwd_grad_kernel(BackwardArgs a, BwdPlan
                 b1[nt] = d;
             }
         }
-        __syncthreads();   // every read of b1m, vt (as v) and dyt of this sub-block is done
+        xe = inner_b1(b1);   // the state entering this sub-block is the one leaving the sub-block before
+        __syncthreads();     // every read of b1m, hs, vt (as v) and dyt of this sub-block is done
         store_out_tile<IO, NTC, LD>(static_cast<IO*>(a.dv) + (rowb + (size_t)t0 * a.K) * P + col0, rs, n, vt, lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) b1m[(4 * g + r) * LD + nt * 16 + i] = b1[nt][r];   // rows >= 2m are zero
-        cur ^= 1;
+            for (int r = 0; r < 4; ++r)   // rows >= 2m of b1 are zero: they rewrite the zero row
+                b1m[min(4 * g + r, ROWS) * LD + nt * 16 + i] = b1[nt][r];
         __syncthreads();
     }
 
@@ -977,11 +989,10 @@ hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
 
 template <int M, typename IO>
 hipError_t launch_m(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
-    switch (pl.P) {
+    switch (pl.P / pl.nslice) {   // columns per slice
         case 16: return launch_all<M, 16, IO>(a, pl, s);
         case 32: return launch_all<M, 32, IO>(a, pl, s);
-        case 64:
-        case 128: return launch_all<M, 64, IO>(a, pl, s);
+        case 64: return launch_all<M, 64, IO>(a, pl, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -999,20 +1010,21 @@ hipError_t launch_io(const BackwardArgs& a, int m, const BwdPlan& pl, hipStream_
 
 }  // namespace
 
-// Resident waves of the gradient kernel on the whole GPU (256 CUs x 4 SIMDs x its occupancy:
-// two waves per SIMD, one for m = 8 with 64-column slices).
-static int grad_wave_slots(int m, int P) { return (m == 8 && P >= 64) ? 1024 : 2048; }
+// Resident waves of the gradient kernel on the whole GPU: 256 CUs x 4 SIMDs x two waves.
+constexpr int GRAD_WAVE_SLOTS = 2048;
 
 BwdPlan plan_backward(int B, int L, int K, int K_T, int m, int P) {
     BwdPlan pl{};
     pl.P = P;
-    pl.nslice = P > 64 ? P / 64 : 1;
+    // columns per wave: 64, or 32 with eight modes (whose states and products need the room)
+    const int width = P < 64 ? P : (m == 8 ? 32 : 64);
+    pl.nslice = P / width;
     pl.nseq = B * K_T;
     pl.L = L;
     // segments per sequence: the waves (sequence, segment, slice) fill whole rounds of the
     // gradient kernel's resident slots, with segments of at most MAX_BWD_SUBBLOCKS sub-blocks
     const long long per = (long long)pl.nseq * pl.nslice;
-    const long long slots = grad_wave_slots(m, P);
+    const long long slots = GRAD_WAVE_SLOTS;
     long long ls = SB;
     for (long long r = 1;; ++r) {
         long long nseg = per > 0 ? (slots * r) / per : 1;
@@ -1036,7 +1048,7 @@ size_t backward_workspace_bytes(int B, int L, int K, int K_T, int m, int P) {
     add(segs * pl.nsb * state);          // ck
     add(segs * state);                   // sa
     add(segs * state);                   // hin
-    add(segs * pl.nsb * m * 2);          // ltr
+    add(segs * pl.nsb * m * 2);          // tpf
     add(segs * m * 2);                   // lam
     add(segs * pl.nslice * (4 * m + 1)); // pp
     add((size_t)pl.nseq * L * 4);        // pc
@@ -1056,7 +1068,7 @@ void bind_backward_workspace(BwdPlan& pl, void* ws, int m) {
     pl.ck = take(segs * pl.nsb * state);
     pl.sa = take(segs * state);
     pl.hin = take(segs * state);
-    pl.ltr = reinterpret_cast<float2*>(take(segs * pl.nsb * m * 2));
+    pl.tpf = reinterpret_cast<float2*>(take(segs * pl.nsb * m * 2));
     pl.lam = reinterpret_cast<float2*>(take(segs * m * 2));
     pl.pp = take(segs * pl.nslice * (4 * m + 1));
     pl.pc = reinterpret_cast<float4*>(take((size_t)pl.nseq * pl.L * 4));

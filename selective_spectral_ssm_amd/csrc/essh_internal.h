@@ -120,7 +120,7 @@ struct BackwardArgs {
 //   ck   [nseq][nseg][nsb][2m][P]  local state (from a zero entering state) after each sub-block
 //   sa   [nseq][nseg][2m][P]       local adjoint aggregate, then the arriving adjoint
 //   hin  [nseq][nseg][2m][P]       entering state of each segment
-//   ltr  [nseq][nseg][nsb][m]      sub-block transfers lambda_j^n e^{-q(n-1)} (complex)
+//   tpf  [nseq][nseg][nsb][m]      transfer from the segment start to each sub-block's start (complex)
 //   lam  [nseq][nseg][m]           segment transfers (complex)
 //   pp   [nseq][nseg][nslice][4m+1] mode-table partials (Omega_j, Gamma_j, trace)
 //   pc   [nseq][L]                 channel-major controls (delta, g_w, g_r, 0)
@@ -131,7 +131,7 @@ struct BwdPlan {
     float* ck;
     float* sa;
     float* hin;
-    float2* ltr;
+    float2* tpf;
     float2* lam;
     float* pp;
     float4* pc;
