@@ -41,6 +41,8 @@
 //   4. bwd_param_kernel sums the mode-table partials;
 // around them bwd_pack_kernel makes a channel-major copy of the controls and bwd_unpack_kernel
 // turns the channel-major control gradients (summed over column slices) back into [B, L, K].
+// Every exponential is of a non-positive clock difference, evaluated with the hardware exp2
+// (__expf): its relative error stays within a few units of fp32 rounding times the exponent.
 // MFMA layouts (16x16x4 f32): A operand lane l = A[l % 16][l / 16], B operand lane l =
 // B[l / 16][l % 16], result lane l register r = D[4 (l / 16) + r][l % 16].  A state [2m rows]
 // [columns] is held as 16-column result tiles (rows 4g..4g+3 of column i in lane (g, i)).
@@ -225,7 +227,7 @@ __device__ __forceinline__ void store_out_tile(IO* dst, size_t stride, int n, co
 template <int M>
 __device__ __forceinline__ float2 sub_transfer(const Tables<M>& T, int j, int n, float qe) {
     if (j >= M) return make_float2(0.f, 0.f);
-    const float e = expf(-qe);
+    const float e = __expf(-qe);
     const float2 p = T.pw[n][j];
     return make_float2(e * p.x, e * p.y);
 }
@@ -348,7 +350,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             const int s = 4 * kk + g;
             const bool ok = i < ROWS && s < n;
             const float2 p = T.pw[ok ? n - 1 - s : 0][i < ROWS ? i >> 1 : 0];
-            const float w = ((i & 1) ? p.y : p.x) * expf(apos[0][s] - c.qe) * apos[1][s];
+            const float w = ((i & 1) ? p.y : p.x) * __expf(apos[0][s] - c.qe) * apos[1][s];
             wa[kk] = ok ? w : 0.f;
         }
         float* ck = pl.ck + ((segi * pl.nsb + sb) * ROWS) * (size_t)pl.P + col0;
@@ -410,7 +412,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             const int u = 4 * kk + g;
             const bool ok = i < ROWS && u < n;
             const float2 cp = T.cpw[u + 1][i < ROWS ? i >> 1 : 0];
-            const float w = apos[1][u] * expf(-apos[0][u]) * ((i & 1) ? -cp.y : cp.x);
+            const float w = apos[1][u] * __expf(-apos[0][u]) * ((i & 1) ? -cp.y : cp.x);
             ca[kk] = ok ? w : 0.f;
         }
 #pragma unroll
@@ -670,8 +672,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             pos[0][i] = c.q;
             pos[1][i] = c.gr;
             pos[2][i] = c.gw;
-            pos[3][i] = i < n ? expf(-c.q) : 0.f;
-            pos[4][i] = i < n ? expf(c.q - c.qe) : 0.f;
+            pos[3][i] = i < n ? __expf(-c.q) : 0.f;
+            pos[4][i] = i < n ? __expf(c.q - c.qe) : 0.f;
         }
         if (sb > 0) {   // inputs of the next sub-block (the one before) go out now
             const int t1 = t0 - SB, n1 = sub_n(sb - 1);
@@ -689,8 +691,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         for (int r = 0; r < 4; ++r) {
             const int aa = 4 * g + r;
             const float qa = pos[0][aa];
-            eS[r] = (aa >= i && aa < n) ? expf(c.q - qa) : 0.f;
-            GT[aa * LM + i] = (i >= aa && i < n) ? c.gr * expf(qa - c.q) * T.psi[i >= aa ? i - aa : 0] : 0.f;
+            eS[r] = (aa >= i && aa < n) ? __expf(c.q - qa) : 0.f;
+            GT[aa * LM + i] = (i >= aa && i < n) ? c.gr * __expf(qa - c.q) * T.psi[i >= aa ? i - aa : 0] : 0.f;
             const bool rok = i < ROWS;
             const int jj = rok ? i >> 1 : 0;
             const float2 cp = T.cpw[aa + 1][jj];
