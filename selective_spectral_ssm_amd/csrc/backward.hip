@@ -974,13 +974,15 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(BackwardArgs a, BwdPlan 
     }
 }
 
-template <int M, int NTC, typename IO>
+// NTC: columns per wave of the gradient kernel; NTA: of the aggregate kernel (which has the
+// registers for 64 also with eight modes)
+template <int M, int NTC, int NTA, typename IO>
 hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     const dim3 pgrid((unsigned)((a.L + PK_T - 1) / PK_T), (unsigned)((a.K_T + PK_K - 1) / PK_K), (unsigned)a.B);
     hipLaunchKernelGGL((bwd_pack_kernel<IO>), pgrid, dim3(256), 0, s, a, pl);
     const dim3 grid((unsigned)pl.nseg, (unsigned)pl.nslice, (unsigned)pl.nseq);
-    const dim3 grid2((unsigned)pl.nseg, (unsigned)(2 * pl.nslice), (unsigned)pl.nseq);   // state and adjoint chains
-    hipLaunchKernelGGL((bwd_agg_kernel<M, NTC, IO>), grid2, dim3(64), 0, s, a, pl);
+    const dim3 grid2((unsigned)pl.nseg, (unsigned)(2 * (pl.P / NTA)), (unsigned)pl.nseq);   // state and adjoint chains
+    hipLaunchKernelGGL((bwd_agg_kernel<M, NTA, IO>), grid2, dim3(64), 0, s, a, pl);
     const size_t nthr = (size_t)pl.nseq * M * pl.P;
     hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_grad_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
@@ -992,9 +994,9 @@ hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
 template <int M, typename IO>
 hipError_t launch_m(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     switch (pl.P / pl.nslice) {   // columns per slice
-        case 16: return launch_all<M, 16, IO>(a, pl, s);
-        case 32: return launch_all<M, 32, IO>(a, pl, s);
-        case 64: return launch_all<M, 64, IO>(a, pl, s);
+        case 16: return launch_all<M, 16, 16, IO>(a, pl, s);
+        case 32: return pl.P >= 64 ? launch_all<M, 32, 64, IO>(a, pl, s) : launch_all<M, 32, 32, IO>(a, pl, s);
+        case 64: return launch_all<M, 64, 64, IO>(a, pl, s);
         default: return hipErrorInvalidValue;
     }
 }
