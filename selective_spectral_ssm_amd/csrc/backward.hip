@@ -46,7 +46,7 @@
 // MFMA layouts (16x16x4 f32): A operand lane l = A[l % 16][l / 16], B operand lane l =
 // B[l / 16][l % 16], result lane l register r = D[4 (l / 16) + r][l % 16].  A state [2m rows]
 // [columns] is held as 16-column result tiles (rows 4g..4g+3 of column i in lane (g, i)).
-#include "essh_internal.h"
+#include "backward.h"
 
 namespace essh {
 namespace {

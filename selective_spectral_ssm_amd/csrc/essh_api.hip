@@ -4,7 +4,7 @@
 // HIP kernels of prefill_chunk.hip, prefill_seq.hip and decode.hip.
 #include <stdint.h>
 
-#include "essh_internal.h"
+#include "backward.h"
 
 using namespace essh;
 
