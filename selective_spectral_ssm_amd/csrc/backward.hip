@@ -36,7 +36,8 @@
 //   1. bwd_agg_kernel   local state chain from zero over the segment (checkpoints after every
 //                       sub-block) and sub-block transfers in one wave, the local adjoint chain
 //                       from zero in another;
-//   2. bwd_scan_kernel  scan over segments: entering states and arriving adjoints;
+//   2. bwd_scan_kernel  scan over segments: entering states and arriving adjoints, each
+//                       direction in threads of its own;
 //   3. bwd_grad_kernel  the sub-blocks of each segment in reverse, every gradient above;
 //   4. bwd_param_kernel sums the mode-table partials;
 // around them bwd_pack_kernel makes a channel-major copy of the controls and bwd_unpack_kernel
@@ -446,6 +447,7 @@ constexpr int SCAN_BATCH = 8;
 template <int M>
 __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan pl) {
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool adjoint = blockIdx.y == 1;   // the two directions run in separate threads
     const int P = pl.P;
     if (tid >= (size_t)pl.nseq * M * P) return;
     const int p = (int)(tid % P);
@@ -456,41 +458,45 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a, BwdPlan p
     const size_t sidx = ((((size_t)b * a.K + k) * M + j) * 2) * P + p;   // state [B][K][m][2][P]
     const size_t seg0 = (size_t)seq * pl.nseg;
 
-    float hr = 0.f, hi = 0.f;
-    if (a.state_in) {
-        hr = a.state_in[sidx];
-        hi = a.state_in[sidx + P];
-    }
-    for (int sbase = 0; sbase < pl.nseg; sbase += SCAN_BATCH) {
-        float ar[SCAN_BATCH], ai[SCAN_BATCH];
-        float2 t[SCAN_BATCH];
+    if (!adjoint) {   // entering state of every segment, first segment first
+        float hr = 0.f, hi = 0.f;
+        if (a.state_in) {
+            hr = a.state_in[sidx];
+            hi = a.state_in[sidx + P];
+        }
+        for (int sbase = 0; sbase < pl.nseg; sbase += SCAN_BATCH) {
+            float ar[SCAN_BATCH], ai[SCAN_BATCH];
+            float2 t[SCAN_BATCH];
 #pragma unroll
-        for (int q = 0; q < SCAN_BATCH; ++q) {
-            const int seg = sbase + q;
-            ar[q] = ai[q] = 0.f;
-            t[q] = make_float2(0.f, 0.f);
-            if (seg < pl.nseg) {
-                const int len = min(pl.Ls, a.L - seg * pl.Ls), nsb = (len + SB - 1) / SB;
-                const float* agg = pl.ck + (((seg0 + seg) * pl.nsb + nsb - 1) * ROWS + 2 * j) * (size_t)P + p;
-                ar[q] = agg[0];
-                ai[q] = agg[P];
-                t[q] = pl.lam[(seg0 + seg) * M + j];
+            for (int q = 0; q < SCAN_BATCH; ++q) {
+                const int seg = sbase + q;
+                ar[q] = ai[q] = 0.f;
+                t[q] = make_float2(0.f, 0.f);
+                if (seg < pl.nseg) {
+                    const int len = min(pl.Ls, a.L - seg * pl.Ls), nsb = (len + SB - 1) / SB;
+                    const float* agg = pl.ck + (((seg0 + seg) * pl.nsb + nsb - 1) * ROWS + 2 * j) * (size_t)P + p;
+                    ar[q] = agg[0];
+                    ai[q] = agg[P];
+                    t[q] = pl.lam[(seg0 + seg) * M + j];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < SCAN_BATCH; ++q) {
+                const int seg = sbase + q;
+                if (seg < pl.nseg) {
+                    float* hin = pl.hin + ((seg0 + seg) * ROWS + 2 * j) * (size_t)P + p;
+                    hin[0] = hr;
+                    hin[P] = hi;
+                    const float nr = t[q].x * hr - t[q].y * hi + ar[q];
+                    const float ni = t[q].y * hr + t[q].x * hi + ai[q];
+                    hr = nr;
+                    hi = ni;
+                }
             }
         }
-#pragma unroll
-        for (int q = 0; q < SCAN_BATCH; ++q) {
-            const int seg = sbase + q;
-            if (seg < pl.nseg) {
-                float* hin = pl.hin + ((seg0 + seg) * ROWS + 2 * j) * (size_t)P + p;
-                hin[0] = hr;
-                hin[P] = hi;
-                const float nr = t[q].x * hr - t[q].y * hi + ar[q];
-                const float ni = t[q].y * hr + t[q].x * hi + ai[q];
-                hr = nr;
-                hi = ni;
-            }
-        }
+        return;
     }
+    // arriving adjoint of every segment, last segment first
     float br = 0.f, bi = 0.f;
     if (a.dstate_out) {
         br = a.dstate_out[sidx];
@@ -984,7 +990,7 @@ hipError_t launch_all(const BackwardArgs& a, const BwdPlan& pl, hipStream_t s) {
     const dim3 grid2((unsigned)pl.nseg, (unsigned)(2 * (pl.P / NTA)), (unsigned)pl.nseq);   // state and adjoint chains
     hipLaunchKernelGGL((bwd_agg_kernel<M, NTA, IO>), grid2, dim3(64), 0, s, a, pl);
     const size_t nthr = (size_t)pl.nseq * M * pl.P;
-    hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, a, pl);
+    hipLaunchKernelGGL((bwd_scan_kernel<M>), dim3((unsigned)((nthr + 255) / 256), 2), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_grad_kernel<M, NTC, IO>), grid, dim3(64), 0, s, a, pl);
     hipLaunchKernelGGL((bwd_param_kernel<M>), dim3((unsigned)a.K_T), dim3(256), 0, s, a, pl);
     hipLaunchKernelGGL(bwd_unpack_kernel, pgrid, dim3(256), 0, s, a, pl);
