@@ -172,3 +172,55 @@ def test_segmented_prefill_needs_a_workspace(lib):
     assert _call_ws(d, None, 0) == essh.ESSH_ERR_WORKSPACE
     assert _call_ws(d, FAKE * 16, need - 1) == essh.ESSH_ERR_WORKSPACE
     assert _call_ws(d, FAKE * 16 + 16, need) == essh.ESSH_ERR_WORKSPACE     # not 256-byte aligned
+
+
+def _call_bwd(dims, ws=FAKE * 16, ws_bytes=None, **over):
+    names = ("v", "delta", "g_w", "g_r", "rho", "theta", "c", "zl", "state_in", "dy", "dstate_out", "dv", "ddelta",
+             "dg_w", "dg_r", "drho", "dtheta", "dc", "dzl", "dstate_in")
+    p = {k: FAKE for k in names}
+    for k in ("zl", "state_in", "dstate_out", "dzl", "dstate_in"):
+        p[k] = None
+    p.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    if ws_bytes is None:
+        ws_bytes = essh.essh_prefill_backward_workspace_bytes(dims)
+    return essh.lib().essh_mixer_prefill_backward(ctypes.byref(dims), *[vp(p[k]) for k in names], vp(ws), ws_bytes,
+                                                  None)
+
+
+def test_backward_validation(lib):
+    """Host-side checks of the backward entry point: nothing is launched on these paths."""
+    d = essh.make_dims(8, 2048, 24, 4, 64, 24, 0)
+    need = essh.essh_prefill_backward_workspace_bytes(d)
+    assert need > 0
+    pm = essh.make_dims(8, 2048, 24, 4, 64, 24, 0, per_mode=True)
+    assert essh.essh_prefill_backward_workspace_bytes(pm) == 0
+    assert _call_bwd(pm, ws_bytes=need) == essh.ESSH_ERR_UNSUPPORTED                 # per-mode controls
+    for name in ("v", "delta", "g_w", "g_r", "rho", "theta", "c", "dy", "dv", "ddelta", "dg_w", "dg_r", "drho",
+                 "dtheta", "dc"):
+        assert _call_bwd(d, **{name: None}) == essh.ESSH_ERR_INVALID_ARG, name       # required pointers
+    for name, addr in (("v", FAKE + 2), ("dy", FAKE + 8), ("dv", FAKE + 4), ("ddelta", FAKE + 2),
+                       ("dstate_in", FAKE + 2), ("zl", FAKE + 1)):
+        assert _call_bwd(d, **{name: addr}) == essh.ESSH_ERR_INVALID_ARG, name       # misaligned
+    assert _call_bwd(d, ws=None) == essh.ESSH_ERR_WORKSPACE
+    assert _call_bwd(d, ws_bytes=need - 1) == essh.ESSH_ERR_WORKSPACE
+    assert _call_bwd(d, ws=FAKE * 16 + 16) == essh.ESSH_ERR_WORKSPACE                # not 256-byte aligned
+    bad = essh.make_dims(8, 2048, 24, 4, 64, 25, 0)
+    assert _call_bwd(bad, ws_bytes=need) == essh.ESSH_ERR_INVALID_ARG                # K_T > K
+    wide = essh.make_dims(4096, 16, 32, 4, 64, 32, 0)                                 # B K_T > 65535
+    assert _call_bwd(wide) == essh.ESSH_ERR_UNSUPPORTED
+    odd = essh.make_dims(8, 2048, 24, 3, 64, 24, 0)
+    assert _call_bwd(odd, ws_bytes=need) == essh.ESSH_ERR_UNSUPPORTED                # m outside the set
+
+
+def test_backward_workspace_covers_its_arrays(lib):
+    """The workspace holds at least the state checkpoints (2 m P fp32 per 16 positions and
+    sequence), the channel-major controls and the control gradients (16 bytes per position and
+    sequence each, per column slice for the gradients)."""
+    for B, L, K, m, P in [(8, 2048, 24, 4, 64), (16, 2048, 32, 8, 128), (1, 131072, 24, 4, 64), (2, 37, 3, 2, 16)]:
+        d = essh.make_dims(B, L, K, m, P, K, 0)
+        need = essh.essh_prefill_backward_workspace_bytes(d)
+        nseq = B * K
+        slices = P // 32 if (m == 8 and P >= 64) else max(1, P // 64)
+        ck = nseq * ((L + 15) // 16) * 2 * m * P * 4
+        assert need >= ck + nseq * L * 16 * (1 + slices), (B, L, K, m, P)
