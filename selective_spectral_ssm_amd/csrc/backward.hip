@@ -91,6 +91,16 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
+// Barrier for the one-wave workgroups of the aggregate and gradient kernels: it orders LDS
+// accesses only.  __syncthreads() would also wait for every outstanding global load and store
+// of the wave, which turns the next sub-block's prefetch into a full memory round trip.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int M> struct Tables {
     float2 pw[SB + 1][M];     // lambda_j^tau
     float2 cpw[SB + 1][M];    // c_j lambda_j^tau
@@ -344,7 +354,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             tv.load(vsrc + (size_t)t1 * rs, rs, sub_n(sb + 1), lane);
         }
         const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
-        __syncthreads();
+        lds_barrier();
         float wa[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -376,7 +386,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         }
         tr0 = cmul(l0, tr0);
         tr1 = cmul(l1, tr1);
-        __syncthreads();
+        lds_barrier();
     }
     if (sl == 0 && i == 0) {
         if (2 * g < M) pl.lam[segi * M + 2 * g] = tr0;
@@ -406,7 +416,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             tv.load(dsrc + (size_t)t1 * rs, rs, sub_n(sb - 1), lane);
         }
         const float2 l0 = sub_transfer<M>(T, 2 * g, n, c.qe), l1 = sub_transfer<M>(T, 2 * g + 1, n, c.qe);
-        __syncthreads();
+        lds_barrier();
         float ca[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -427,7 +437,7 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             for (int kk = 0; kk < 4; ++kk) d = mfma4(ca[kk], tile[(4 * kk + g) * LD + nt * 16 + i], d);
             bt[nt] = d;
         }
-        __syncthreads();
+        lds_barrier();
     }
     float* sa = pl.sa + segi * ROWS * (size_t)pl.P + col0;
 #pragma unroll
@@ -584,7 +594,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         const float xr = h[0], xi = h[P];
         hinr[e] = ok ? make_float2(xr, xi) : make_float2(0.f, 0.f);
     }
-    __syncthreads();
+    lds_barrier();
     f32x4 b1[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -649,7 +659,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         load_ck(ckr, nsb);
         load_tp(tpr, nsb);
         put_state(ckr, tpr);
-        __syncthreads();
+        lds_barrier();
         xe = inner_b1(b1);
     }
     float2 ckn[CKE], tpn[CKE];
@@ -663,7 +673,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
         tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
     }
-    __syncthreads();
+    lds_barrier();
 
     f32x4 nacc = f32x4{0.f, 0.f, 0.f, 0.f}, qacc = nacc, racc = nacc;
     float2 zc0 = make_float2(0.f, 0.f), zc1 = zc0;    // modes 2g, 2g + 1
@@ -689,7 +699,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             tvn.load(vsrc + (size_t)t1 * rs, rs, n1, lane);
             tdn.load(dsrc + (size_t)t1 * rs, rs, n1, lane);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- the sub-block's operand matrices; lane (g, i) fills entries (4 g + r, i) ----
         float eS[4];   // e^{-(q(u) - q(s))} at (u = 4 g + r, s = i), u >= s
@@ -708,7 +718,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             WQ[aa * LM + i] = rok ? wq : 0.f;
             WT[aa * LM + i] = rok ? wt : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- products over the value columns: S = dY V^T, Q = dY H0^T, R = V_rev B1^T ----
         f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f}, Q = S, R = S;
@@ -804,7 +814,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             zc1.x += (float)n * a1.x;
             zc1.y += (float)n * a1.y;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- per-position gradients of the controls ----
         {
@@ -862,14 +872,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             }
         }
         xe = inner_b1(b1);   // the state entering this sub-block is the one leaving the sub-block before
-        __syncthreads();     // every read of b1m, hs, vt (as v) and dyt of this sub-block is done
+        lds_barrier();     // every read of b1m, hs, vt (as v) and dyt of this sub-block is done
         store_out_tile<IO, NTC, LD>(static_cast<IO*>(a.dv) + (rowb + (size_t)t0 * a.K) * P + col0, rs, n, vt, lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)   // rows >= 2m of b1 are zero: they rewrite the zero row
                 b1m[min(4 * g + r, ROWS) * LD + nt * 16 + i] = b1[nt][r];
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- mode-table partials of this segment ----
