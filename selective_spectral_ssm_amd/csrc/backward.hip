@@ -720,7 +720,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         }
         lds_barrier();
 
-        // ---- products over the value columns: S = dY V^T, Q = dY H0^T, R = V_rev B1^T ----
+        // ---- products over the value columns: S = dY V^T, and transposed Q = H0 dY^T and
+        //      R = B1 V_rev^T (state rows down, positions across, so that their sums over the
+        //      state rows are sums within a lane and across the four row groups) ----
         f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f}, Q = S, R = S;
         {
             const int ir = i < n ? n - 1 - i : SB - 1;   // reversed row of V for R (row 15 is zero when n < 16)
@@ -735,17 +737,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
                 const float4 r4 = *reinterpret_cast<const float4*>(vt + ir * LD + col);
                 const float4 b4 = *reinterpret_cast<const float4*>(b1m + ri * LD + col);
                 S = mfma4(d4.x, v4.x, S);
-                Q = mfma4(d4.x, h4.x, Q);
-                R = mfma4(r4.x, b4.x, R);
+                Q = mfma4(h4.x, d4.x, Q);
+                R = mfma4(b4.x, r4.x, R);
                 S = mfma4(d4.y, v4.y, S);
-                Q = mfma4(d4.y, h4.y, Q);
-                R = mfma4(r4.y, b4.y, R);
+                Q = mfma4(h4.y, d4.y, Q);
+                R = mfma4(b4.y, r4.y, R);
                 S = mfma4(d4.z, v4.z, S);
-                Q = mfma4(d4.z, h4.z, Q);
-                R = mfma4(r4.z, b4.z, R);
+                Q = mfma4(h4.z, d4.z, Q);
+                R = mfma4(b4.z, r4.z, R);
                 S = mfma4(d4.w, v4.w, S);
-                Q = mfma4(d4.w, h4.w, Q);
-                R = mfma4(r4.w, b4.w, R);
+                Q = mfma4(h4.w, d4.w, Q);
+                R = mfma4(b4.w, r4.w, R);
             }
         }
 
@@ -765,27 +767,26 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         if (i < 4) red[0][4 * g + i] = rsel;
         if (g == 0) red[2][i] = dgw_col;
 
-        // ---- Q: carried-state part of dg_r; R: end-state part of dg_w ----
-        float qsel = 0.f, esel = 0.f;
+        // ---- Q: carried-state part of dg_r; R: end-state part of dg_w.  Lane (g, i) holds
+        //      Q[row = 4 g + r][u = i] and R[row = 4 g + r][s' = i], s' = n - 1 - s ----
+        {
+            const int sr = n - 1 - i, sc = sr >= 0 ? sr : 0;   // position of R column i
+            const float eq = i < n ? pos[3][i] : 0.f;           // e^{-q(i)}
+            const float rw = sr >= 0 ? pos[4][sc] * pos[2][sc] : 0.f;
+            float cs = 0.f, es = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int u = 4 * g + r;
-            const float cs = row_sum16(WQ[u * LM + i] * Q[r]);
-            qsel = i == r ? cs : qsel;
-            qacc[r] += pos[1][u] * pos[3][u] * Q[r];
-            const int s = n - 1 - u;      // R row u is position s
-            const int sc = s >= 0 ? s : 0;
-            const float wt_ = WT[sc * LM + i];
-            const float wr = s >= 0 ? wt_ : 0.f;
-            const float es = row_sum16(wr * R[r]);
-            esel = i == r ? es : esel;
-            const float rw = pos[4][sc] * pos[2][sc];
-            racc[r] += s >= 0 ? rw * R[r] : 0.f;
-        }
-        if (i < 4) {
-            red[1][4 * g + i] = qsel;
-            const int s = n - 1 - (4 * g + i);
-            if (s >= 0) red[3][s] = esel;
+            for (int r = 0; r < 4; ++r) {
+                cs += WQ[i * LM + 4 * g + r] * Q[r];
+                es += WT[sc * LM + 4 * g + r] * R[r];
+                qacc[r] += c.gr * eq * Q[r];
+                racc[r] += rw * R[r];
+            }
+            cs = group_sum4(cs);
+            es = group_sum4(es);
+            if (g == 0) {
+                red[1][i] = cs;
+                if (sr >= 0) red[3][sr] = es;
+            }
         }
 
         // ---- inner products of the arriving adjoint with the entering state (per mode); the
@@ -902,27 +903,29 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
                 om[j][1] += (float)tau * cp.y * nacc[r];
             }
         }
-        if (i < ROWS) {
-            const int jr = i >> 1;
-            const bool im = i & 1;
+        // Qacc[row = 4 g + r][u = i], Racc[row = 4 g + r][s' = i]
+        const int row = 4 * g + r;
+        if (row < ROWS) {
+            const int jr = row >> 1;
+            const bool im = row & 1;
 #pragma unroll
             for (int j = 0; j < M; ++j) {
                 if (j != jr) continue;
-                // Q: (u + 1) c lambda^{u+1} and lambda^{u+1} times (Qre + i Qim)
-                const float2 p = T.pw[u + 1][j], cp = T.cpw[u + 1][j];
+                // Q: (u + 1) c lambda^{u+1} and lambda^{u+1} times (Qre + i Qim), u = i
+                const float2 p = T.pw[i + 1][j], cp = T.cpw[i + 1][j];
                 const float qv = qacc[r];
                 const float2 pq = im ? make_float2(-p.y * qv, p.x * qv) : make_float2(p.x * qv, p.y * qv);
                 const float2 cq = im ? make_float2(-cp.y * qv, cp.x * qv) : make_float2(cp.x * qv, cp.y * qv);
                 gm[j][0] += pq.x;
                 gm[j][1] += pq.y;
-                om[j][0] += (float)(u + 1) * cq.x;
-                om[j][1] += (float)(u + 1) * cq.y;
-                // R: s' lambda^{s'} times (Rre - i Rim), s' = u
-                const float2 pr = T.pw[u][j];
+                om[j][0] += (float)(i + 1) * cq.x;
+                om[j][1] += (float)(i + 1) * cq.y;
+                // R: s' lambda^{s'} times (Rre - i Rim), s' = i
+                const float2 pr = T.pw[i][j];
                 const float rv = racc[r];
                 const float2 rr = im ? make_float2(pr.y * rv, -pr.x * rv) : make_float2(pr.x * rv, pr.y * rv);
-                om[j][0] += (float)u * rr.x;
-                om[j][1] += (float)u * rr.y;
+                om[j][0] += (float)i * rr.x;
+                om[j][1] += (float)i * rr.y;
             }
         }
     }
