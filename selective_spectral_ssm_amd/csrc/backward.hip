@@ -140,24 +140,27 @@ struct SubCtl {
     float gw, gr, q, qe;
 };
 
-// from the channel-major copy of the controls (one 16-byte load per position)
+// from the channel-major copy of the controls (one 16-byte load per position).  The loaded
+// values are kept as they arrive and masked to the sub-block's n positions only where they are
+// used (finish_ctl): a select on a load's result makes the wave wait for it, and for every load
+// issued before it, at the point of the select, which would turn a prefetch into a round trip.
 __device__ __forceinline__ CtlRegs load_ctl_regs(const BackwardArgs& a, const BwdPlan& pl, int seq, int t0, int n,
                                                  int i) {
     CtlRegs c;
-    const bool in = i < n;
-    const float4 x = pl.pc[(size_t)seq * a.L + t0 + (in ? i : 0)];   // clamped: always a valid address
-    c.dl = in ? x.x : 0.f;
-    c.gw = in ? x.y : 0.f;
-    c.gr = in ? x.z : 0.f;
+    const float4 x = pl.pc[(size_t)seq * a.L + t0 + (i < n ? i : 0)];   // clamped: always a valid address
+    c.dl = x.x;
+    c.gw = x.y;
+    c.gr = x.z;
     return c;
 }
 
 __device__ __forceinline__ SubCtl finish_ctl(const CtlRegs& r, int n, int i) {
     SubCtl c;
-    c.gw = r.gw;
-    c.gr = r.gr;
+    const bool in = i < n;
+    c.gw = in ? r.gw : 0.f;
+    c.gr = in ? r.gr : 0.f;
     // inclusive prefix sum within the row of 16 lanes: DPP row shifts, zero from outside the row
-    float q = r.dl;
+    float q = in ? r.dl : 0.f;
     q += dpp_zero<DPP_SHR1>(q);
     q += dpp_zero<DPP_SHR2>(q);
     q += dpp_zero<DPP_SHR4>(q);
@@ -215,25 +218,46 @@ struct TileRegs {
     }
 };
 
+// An output tile: rows [0, n) of a [16][NTC] fp32 LDS tile (row stride LD), converted to the io
+// dtype into registers by read() and stored by whole 16-byte chunks by write().  The two halves
+// are apart so that the stores can go out after the next wait for loads: a wait for loads while
+// stores are outstanding waits for the stores too.
 template <typename IO, int NTC, int LD>
-__device__ __forceinline__ void store_out_tile(IO* dst, size_t stride, int n, const float* tile, int lane) {
-    constexpr int E = 16 / sizeof(IO), CPR = NTC / E, NCH = SB * CPR;
-    for (int idx = lane; idx < NCH; idx += 64) {
-        const int r = idx / CPR, col = (idx - r * CPR) * E;
-        if (r >= n) continue;
-        const float* s = tile + r * LD + col;
-        uint4 w;
-        if constexpr (E == 8) {
-            w.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
-            w.y = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
-            w.z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
-            w.w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
-        } else {
-            w = make_uint4(__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3]));
+struct OutRegs {
+    static constexpr int E = 16 / sizeof(IO);         // elements per 16-byte chunk
+    static constexpr int CPR = NTC / E;               // chunks per row
+    static constexpr int NCH = SB * CPR;              // chunks per tile
+    static constexpr int PER = (NCH + 63) / 64;       // chunks per lane
+    uint4 w[PER];
+
+    __device__ __forceinline__ void read(const float* tile, int lane) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + 64 * e;
+            if (NCH % 64 == 0 || idx < NCH) {
+                const int r = idx / CPR, col = (idx - r * CPR) * E;
+                const float* s = tile + r * LD + col;
+                if constexpr (E == 8) {
+                    w[e].x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
+                    w[e].y = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
+                    w[e].z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
+                    w[e].w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
+                } else {
+                    w[e] = make_uint4(__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]),
+                                      __float_as_uint(s[3]));
+                }
+            }
         }
-        *reinterpret_cast<uint4*>(dst + r * stride + col) = w;
     }
-}
+    __device__ __forceinline__ void write(IO* dst, size_t stride, int n, int lane) const {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = lane + 64 * e;
+            const int r = idx / CPR, col = (idx - r * CPR) * E;
+            if ((NCH % 64 == 0 || idx < NCH) && r < n) *reinterpret_cast<uint4*>(dst + r * stride + col) = w[e];
+        }
+    }
+};
 
 template <int M>
 __device__ __forceinline__ float2 sub_transfer(const Tables<M>& T, int j, int n, float qe) {
@@ -338,6 +362,15 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float2 tr0 = make_float2(1.f, 0.f), tr1 = make_float2(1.f, 0.f);
+    // checkpoint sbx (the state after sub-block sbx, held in st)
+    auto store_ck = [&](int sbx) {
+        float* ck = pl.ck + ((segi * pl.nsb + sbx) * ROWS) * (size_t)pl.P + col0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < ROWS) ck[(size_t)(4 * g + r) * pl.P + nt * 16 + i] = st[nt][r];
+    };
     cr = load_ctl_regs(a, pl, seq, s0, sub_n(0), i);
     tv.load(vsrc + (size_t)s0 * rs, rs, sub_n(0), lane);
     for (int sb = 0; sb < nsb; ++sb) {
@@ -347,6 +380,14 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
         if (g == 0) {
             apos[0][i] = c.q;
             apos[1][i] = c.gw;
+        }
+        // the stores of the sub-block before go out once this one's loads have been waited for
+        // (a wait for loads while stores are outstanding waits for the stores too)
+        if (sb > 0) store_ck(sb - 1);
+        if (sl == 0 && i == 0) {   // transfer from the segment start to this sub-block's start
+            float2* tpf = pl.tpf + (segi * pl.nsb + sb) * M;
+            if (2 * g < M) tpf[2 * g] = tr0;
+            if (2 * g + 1 < M) tpf[2 * g + 1] = tr1;
         }
         if (sb + 1 < nsb) {
             const int t1 = s0 + (sb + 1) * SB;
@@ -364,7 +405,6 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
             const float w = ((i & 1) ? p.y : p.x) * __expf(apos[0][s] - c.qe) * apos[1][s];
             wa[kk] = ok ? w : 0.f;
         }
-        float* ck = pl.ck + ((segi * pl.nsb + sb) * ROWS) * (size_t)pl.P + col0;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 d;
@@ -375,19 +415,12 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BackwardArgs a, BwdPlan pl)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) d = mfma4(wa[kk], tile[(4 * kk + g) * LD + nt * 16 + i], d);
             st[nt] = d;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r < ROWS) ck[(size_t)(4 * g + r) * pl.P + nt * 16 + i] = d[r];
-        }
-        if (sl == 0 && i == 0) {   // transfer from the segment start to this sub-block's start
-            float2* tpf = pl.tpf + (segi * pl.nsb + sb) * M;
-            if (2 * g < M) tpf[2 * g] = tr0;
-            if (2 * g + 1 < M) tpf[2 * g + 1] = tr1;
         }
         tr0 = cmul(l0, tr0);
         tr1 = cmul(l1, tr1);
         lds_barrier();
     }
+    store_ck(nsb - 1);   // nsb >= 1: a segment holds at least one position
     if (sl == 0 && i == 0) {
         if (2 * g < M) pl.lam[segi * M + 2 * g] = tr0;
         if (2 * g + 1 < M) pl.lam[segi * M + 2 * g + 1] = tr1;
@@ -606,16 +639,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
             if (row < ROWS) b1m[row * LD + nt * 16 + i] = x;
         }
 
-    // local checkpoint after sub-block sb - 1 (zero for sb = 0), at this lane's entries
+    // local checkpoint after sub-block sb - 1 at this lane's entries (for sb = 0, where it is
+    // zero, the one after sub-block 0 is read and put_state discards it)
     auto load_ck = [&](float2 (&ckr)[CKE], int sb) {
+        const float* ckb = pl.ck + ((segi * pl.nsb + (sb > 0 ? sb - 1 : 0)) * ROWS) * (size_t)P + col0;
 #pragma unroll
         for (int e = 0; e < CKE; ++e) {
-            const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
-            const bool ok = sb > 0 && (CKN % 64 == 0 || idx < CKN);
-            const int sc = ok ? sb - 1 : 0, jc = ok ? j : 0, cc = ok ? col : 0;   // clamped address
-            const float* ck = pl.ck + ((segi * pl.nsb + sc) * ROWS + 2 * jc) * (size_t)P + col0 + cc;
-            const float xr = ck[0], xi = ck[P];
-            ckr[e] = ok ? make_float2(xr, xi) : make_float2(0.f, 0.f);
+            const int idx = lane + 64 * e;
+            const bool ok = CKN % 64 == 0 || idx < CKN;
+            const int j = ok ? idx / NTC : 0, col = ok ? idx - j * NTC : 0;   // clamped address
+            const int off = 2 * j * P + col;
+            ckr[e] = make_float2(ckb[off], ckb[off + P]);
         }
     };
     // transfer from the segment start to the start of sub-block sb (sb = nsb: the segment end)
@@ -628,14 +662,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
     };
     // true state entering sub-block sb: the checkpoint plus the segment's entering state
     // carried by the transfer from the segment start
-    auto put_state = [&](const float2 (&ckr)[CKE], const float2 (&tpr)[CKE]) {
+    auto put_state = [&](const float2 (&ckr)[CKE], const float2 (&tpr)[CKE], bool has_ck) {
 #pragma unroll
         for (int e = 0; e < CKE; ++e) {
             const int idx = lane + 64 * e, j = idx / NTC, col = idx - j * NTC;
             if (CKN % 64 == 0 || idx < CKN) {
                 const float2 t = tpr[e], h = hinr[e];
-                hs[2 * j * LD + col] = ckr[e].x + t.x * h.x - t.y * h.y;
-                hs[(2 * j + 1) * LD + col] = ckr[e].y + t.x * h.y + t.y * h.x;
+                const float2 ck = has_ck ? ckr[e] : make_float2(0.f, 0.f);
+                hs[2 * j * LD + col] = ck.x + t.x * h.x - t.y * h.y;
+                hs[(2 * j + 1) * LD + col] = ck.y + t.x * h.y + t.y * h.x;
             }
         }
     };
@@ -658,7 +693,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         float2 ckr[CKE], tpr[CKE];
         load_ck(ckr, nsb);
         load_tp(tpr, nsb);
-        put_state(ckr, tpr);
+        put_state(ckr, tpr, nsb > 0);
         lds_barrier();
         xe = inner_b1(b1);
     }
@@ -675,6 +710,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
     }
     lds_barrier();
 
+    // dv of the sub-block after, held in registers until the next wait for loads has passed
+    OutRegs<IO, NTC, LD> dvr;
+    IO* const dvb = static_cast<IO*>(a.dv) + rowb * P + col0;
+    int dv_t0 = -1, dv_n = 0;
+    // and the control gradients of this lane's position of it (gc_t < 0: none)
+    float4* const gcb = pl.gc + ((size_t)sl * pl.nseq + seq) * a.L;
+    float4 gcv = make_float4(0.f, 0.f, 0.f, 0.f);
+    int gc_t = -1;
+
     f32x4 nacc = f32x4{0.f, 0.f, 0.f, 0.f}, qacc = nacc, racc = nacc;
     float2 zc0 = make_float2(0.f, 0.f), zc1 = zc0;    // modes 2g, 2g + 1
 
@@ -683,7 +727,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         const SubCtl c = finish_ctl(crn, n, i);
         tvn.template store<LD>(vt, lane);
         tdn.template store<LD>(dyt, lane);
-        put_state(ckn, tpn);
+        put_state(ckn, tpn, sb > 0);
+        if (dv_t0 >= 0) dvr.write(dvb + (size_t)dv_t0 * rs, rs, dv_n, lane);
+        if (gc_t >= 0) gcb[gc_t] = gcv;
         if (g == 0) {
             pos[0][i] = c.q;
             pos[1][i] = c.gr;
@@ -827,9 +873,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
                 const float o = __shfl_down(cs, off, 16);
                 if (i + off < 16) cs += o;
             }
-            const float ddl = cs - xe;
-            if (g == 0 && i < n)
-                pl.gc[((size_t)sl * pl.nseq + seq) * a.L + t0 + i] = make_float4(ddl, dgw, dgr, 0.f);
+            gcv = make_float4(cs - xe, dgw, dgr, 0.f);
+            gc_t = g == 0 && i < n ? t0 + i : -1;
         }
 
         // ---- dv = g_w (G^T dY + W^T B1), staged in the v tile ----
@@ -874,7 +919,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         }
         xe = inner_b1(b1);   // the state entering this sub-block is the one leaving the sub-block before
         lds_barrier();     // every read of b1m, hs, vt (as v) and dyt of this sub-block is done
-        store_out_tile<IO, NTC, LD>(static_cast<IO*>(a.dv) + (rowb + (size_t)t0 * a.K) * P + col0, rs, n, vt, lane);
+        dvr.read(vt, lane);
+        dv_t0 = t0;
+        dv_n = n;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -882,6 +929,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
                 b1m[min(4 * g + r, ROWS) * LD + nt * 16 + i] = b1[nt][r];
         lds_barrier();
     }
+    dvr.write(dvb + (size_t)dv_t0 * rs, rs, dv_n, lane);   // the first sub-block's (nsb >= 1)
+    if (gc_t >= 0) gcb[gc_t] = gcv;
 
     // ---- mode-table partials of this segment ----
     float om[M][2], gm[M][2];
