@@ -51,6 +51,15 @@ constexpr int WCPY = 8 + 2;
 // global stores then each touch every LDS bank once.
 __device__ __forceinline__ int swz(int r) { return (r & 6) | ((r >> 3) & 1); }
 
+// Every LDS access issued so far has completed, and no instruction is moved across this point
+// in either direction (a stage's last reads before an asynchronous copy overwrites it).
+__device__ __forceinline__ void stage_reads_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int M>
 struct __align__(16) WTables {
     float2 pw[17 + 5][M];         // lambda_j^tau, tau = 0..16; rows 17 + d: lambda_j^{16 d}, d = 0..4
@@ -598,6 +607,12 @@ __global__ void __launch_bounds__(64) wave_prefill_kernel(PrefillArgs a, ScanPla
                 if constexpr (!AGG) {
                     if (blk >= 1) store_y(stv(sp), blk - 1);
                 }
+                // The copies below overwrite stage sp, which the LDS reads just above (the y
+                // rows of block blk-1) and those of the block before still read.  The compiler
+                // takes an asynchronous copy to write only its base address, so it may move
+                // the copies above those reads; a copy that then lands first puts v rows
+                // into y.  The reads are completed and the order is pinned here.
+                stage_reads_done();
                 copy_block(sp, blk + NS - 1);
                 compute_block(stv(s), stc(s), blk);
             }

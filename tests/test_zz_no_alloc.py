@@ -77,7 +77,13 @@ def _compare(prep, got, ref):
     label, w, K_T, kind, dims, need, args = prep
     (y, st), (y_ref, st_ref) = got, ref
     if kind == "exact":
-        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), label
+        diff = y.view(torch.int16) != y_ref.view(torch.int16)
+        if diff.any():
+            idx = diff.nonzero()
+            log(f"{label}: {int(diff.sum())} y elements differ at positions {idx[:, 1].unique()[:16].tolist()}, "
+                f"channels {idx[:, 2].unique().tolist()}; max |dy| "
+                f"{float((y.float() - y_ref.float()).abs().max()):.3e}")
+        assert not diff.any(), label
         assert torch.equal(st, st_ref), label
     else:
         ey = block_err(to_host_f64(y)[:, :, :K_T], to_host_f64(y_ref)[:, :, :K_T], chan_axis=2)
