@@ -172,7 +172,8 @@ essh_status essh_mixer_prefill(const essh_dims* d,
  * host threads) race and give invalid results; order them.
  * Returns ESSH_ERR_SCRATCH, before launching anything, when
  * essh_prefill_workspace_bytes(d) exceeds ESSH_NOALLOC_SCRATCH_BYTES (for
- * example 1 x 131072 positions at K_T = 24, m = 4, P = 64 needs about 38 MB).
+ * example 1 x 131072 positions at K_T = 24, m = 4, P = 64 needs about 51 MB;
+ * at K_T = 12, about 20 MB).
  */
 essh_status essh_mixer_prefill_noalloc(const essh_dims* d,
                                        const void* v, const float* delta, const void* g_w, const void* g_r,

@@ -134,17 +134,30 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
     if (p.nseq == 0 || p.nchunks == 0) return p;
     constexpr int SPLIT_MAX_SEQ = 32;
     if (p.nseq <= SPLIT_MAX_SEQ && wave_supported(m, P, Lc, ESSH_BF16, per_mode)) {
-        // Few, long sequences with P = 64: the three-launch scan over about WAVE_TARGET
-        // segments with one wave per (sequence, segment) (prefill_wave.hip).
-        constexpr int WAVE_TARGET = 3072;
+        // Few, long sequences with P = 64: the three-launch scan with one wave per (sequence,
+        // segment) (prefill_wave.hip).  The segment length is picked between the shortest the
+        // segment scan composes and twice that, to fill the last round of WAVE_SLOTS resident
+        // waves (eight one-wave workgroups per CU on 256 CUs) as fully as possible, the shorter
+        // length on a tie: a round that is only started (say 4104 waves on 2048 slots) costs
+        // almost a whole round's time, while more and shorter segments cost the aggregate and
+        // segment-scan launches little.
+        constexpr long long WAVE_SLOTS = 2048;
         p.wave = 1;
         int seg_chunks = p.nchunks;
         p.mode = SCAN_SPLIT;
         {
-            const long long want = ((long long)p.nchunks * p.nseq + WAVE_TARGET - 1) / WAVE_TARGET;
             const int max_seg = 1 + SCAN_PER * (1024 / P);
-            const int min_chunks = (p.nchunks + max_seg - 1) / max_seg;
-            seg_chunks = (int)(want > min_chunks ? want : min_chunks);
+            const int lo = (p.nchunks + max_seg - 1) / max_seg;
+            double best = -1.0;
+            for (int c = lo; c <= 2 * lo && c <= p.nchunks; ++c) {
+                const long long waves = (long long)p.nseq * ((p.nchunks + c - 1) / c);
+                const long long rounds = (waves + WAVE_SLOTS - 1) / WAVE_SLOTS;
+                const double fill = (double)waves / (double)(rounds * WAVE_SLOTS);
+                if (fill > best + 1e-9) {
+                    best = fill;
+                    seg_chunks = c;
+                }
+            }
         }
         if (seg_chunks < 1) seg_chunks = 1;
         if (seg_chunks > p.nchunks) seg_chunks = p.nchunks;

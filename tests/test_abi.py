@@ -76,7 +76,7 @@ def test_noalloc_scratch_limit(lib):
     bad = essh.make_dims(1, 2048, 24, 4, 64, 25, 64)   # K_T > K
     assert lib.essh_mixer_prefill_noalloc(ctypes.byref(bad), *p, None, None, None, ctypes.c_void_p(FAKE),
                                           None, None) == essh.ESSH_ERR_INVALID_ARG
-    fits = essh.make_dims(1, 131072, 24, 4, 64, 18, 128)
+    fits = essh.make_dims(1, 131072, 24, 4, 64, 12, 128)
     assert 0 < essh.essh_prefill_workspace_bytes(fits) <= essh.NOALLOC_SCRATCH_BYTES
 
 
