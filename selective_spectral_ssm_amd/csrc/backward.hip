@@ -80,10 +80,22 @@ __device__ __forceinline__ float row_sum16(float x) {
     x += dpp_zero<DPP_MIRROR>(x);
     return x;
 }
-// sum over the four row groups (equal lane & 15)
+// sum over the four row groups (equal lane & 15), in VALU lane swaps (no LDS round trip): with
+// the same value in both operands, v_permlane16_swap hands each row the row beside it (rows 0
+// and 1, rows 2 and 3) and v_permlane32_swap each half the other half
 __device__ __forceinline__ float group_sum4(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// inclusive suffix sum within each row of 16 lanes (row_shl:n reads lane i + n of the row,
+// zero past its end)
+__device__ __forceinline__ float row_suffix16(float x) {
+    x += dpp_zero<0x101>(x);
+    x += dpp_zero<0x102>(x);
+    x += dpp_zero<0x104>(x);
+    x += dpp_zero<0x108>(x);
     return x;
 }
 __device__ __forceinline__ float wave_sum64(float x) { return group_sum4(row_sum16(x)); }
@@ -166,7 +178,13 @@ __device__ __forceinline__ SubCtl finish_ctl(const CtlRegs& r, int n, int i) {
     q += dpp_zero<DPP_SHR4>(q);
     q += dpp_zero<DPP_SHR8>(q);
     c.q = q;
-    c.qe = __shfl(q, n - 1, 16);
+    // q(n - 1) of each row, read from its lane by lane index (n is the same in every lane)
+    const int g = (threadIdx.x & 63) >> 4;
+    const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q), n - 1));
+    const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q), 15 + n));
+    const float q2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q), 31 + n));
+    const float q3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q), 47 + n));
+    c.qe = g == 0 ? q0 : g == 1 ? q1 : g == 2 ? q2 : q3;
     return c;
 }
 
@@ -867,12 +885,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         {
             const float dgr = i < n ? red[0][i] + red[1][i] : 0.f;
             const float dgw = i < n ? red[2][i] + red[3][i] : 0.f;
-            float cs = i < n ? c.gw * dgw - c.gr * dgr : 0.f;   // dL/dq(i)
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                const float o = __shfl_down(cs, off, 16);
-                if (i + off < 16) cs += o;
-            }
+            // sum of dL/dq over positions i .. n - 1 of the sub-block
+            const float cs = row_suffix16(i < n ? c.gw * dgw - c.gr * dgr : 0.f);
             gcv = make_float4(cs - xe, dgw, dgr, 0.f);
             gc_t = g == 0 && i < n ? t0 + i : -1;
         }
