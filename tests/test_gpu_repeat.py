@@ -1,10 +1,13 @@
-"""Repeatability of the three-launch prefill for few, long sequences (needs an MI355X).
+"""Repeatability of every entry point (needs an MI355X): identical calls, identical bits.
 
 The one-wave kernel stages each block of v in LDS by asynchronous global-to-LDS copies into a
 ring of stages, stages y in place over it, and reads y back before the copies of a later block
 overwrite the stage.  The copies must not overtake those reads: if they did, a few calls in a
 hundred would store v rows (the segment's last row, which copies past its end repeat) as y.
-Identical calls must therefore give identical y and state, bit for bit, every time.
+Identical calls must therefore give identical y and state, bit for bit, every time.  The other
+entry points (the look-back, whole-sequence, four-wave three-launch, per-mode and fp32 prefill
+forms, the decode step and the backward pass) are held to the same bar: none of them lets the
+order of arrival of other workgroups' results enter its arithmetic.
 """
 from __future__ import annotations
 
@@ -59,3 +62,93 @@ def test_three_launch_prefill_is_repeatable(over, K_T, calls):
             idx = diff.nonzero()
             bad.append((r, int(diff.sum()), idx[:, 1].unique()[:8].tolist(), idx[:, 2].unique().tolist()))
     assert not bad, f"calls that differ from the first (call, elements, positions, channels): {bad[:5]}"
+
+
+def _same(a, b):
+    import torch
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a, b)
+
+
+def _repeat(fn, calls):
+    """Run fn `calls` times; return the indices of the calls whose outputs differ from the first."""
+    import torch
+    ref, bad = None, []
+    for r in range(calls):
+        outs = [o.clone() for o in fn() if o is not None]
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = outs
+        elif not all(_same(a, b) for a, b in zip(outs, ref)):
+            bad.append(r)
+    return bad
+
+
+# the other prefill forms: look-back (370M-class), whole sequences (1.5B-class at K_T = 32), the
+# four-wave three-launch scan (1.5B-class at K_T = 8), per-mode controls, fp32 io
+PREFILL_FORMS = [("lookback_kt24", 1, dict(B=2, L=700), 24, False, 100),
+                 ("whole_kt32", 2, dict(B=16, L=300), 32, False, 50),
+                 ("three_launch_4wave_kt8", 2, dict(B=2, L=1500), 8, False, 50),
+                 ("per_mode_kt24", 1, dict(B=2, L=700), 24, True, 50),
+                 ("f32", 0, dict(L=300), 8, False, 50)]
+
+
+@pytest.mark.parametrize("label,wi,over,K_T,per_mode,calls", PREFILL_FORMS, ids=[c[0] for c in PREFILL_FORMS])
+def test_prefill_forms_are_repeatable(label, wi, over, K_T, per_mode, calls):
+    import numpy as np
+    from selective_spectral_ssm_amd import essh
+    from tests.gpu_util import to_dev
+    w = I.workload(wi, **over)
+    d = device_inputs(I.make_prefill_inputs(w, per_mode=per_mode))
+    rng = np.random.default_rng(5)
+    zl = to_dev(rng.uniform(0, 1, (w.K, w.m)).astype(np.float32))
+    s_in = to_dev(rng.standard_normal((w.B, w.K, w.m, 2, w.P)).astype(np.float32))
+    pf = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], K_T, w.Lc, s_in, True,
+                      None, None, zl)
+
+    def go():
+        pf.y.zero_()
+        pf.state_out.zero_()
+        return pf.run()
+    log(f"{label}: {calls} identical calls")
+    bad = _repeat(go, calls)
+    pf.check()
+    assert not bad, f"{label}: calls {bad[:8]} differ from the first"
+
+
+def test_decode_and_backward_are_repeatable():
+    import numpy as np
+    import torch
+    from selective_spectral_ssm_amd import essh
+    from tests.gpu_util import to_dev
+    # decode step, 24 layers of the 1.5B-class shape, from the same state every call
+    w = I.workload(3)
+    x = I.make_decode_inputs(w, n_steps=1, context=16)
+    st0 = to_dev(np.random.default_rng(9).standard_normal((w.layers, 1, w.K, w.m, 2, w.P)).astype(np.float32))
+    dv = {k: to_dev(x["step_" + k][0]) for k in ("v", "delta", "g_w", "g_r")}
+    pr = {k: to_dev(x[k]) for k in ("rho", "theta", "c")}
+
+    def dec():
+        st = st0.clone()
+        y = torch.zeros_like(dv["v"])   # channels past K_T are never written
+        essh.decode_step(st, dv["v"], dv["delta"], dv["g_w"], dv["g_r"], pr["rho"], pr["theta"], pr["c"], K_T=24, y=y)
+        return y, st
+    log("decode: 100 identical steps")
+    assert not _repeat(dec, 100), "decode steps differ"
+    # backward pass with every optional input
+    wb = I.workload(1, B=2, L=300, K=6)
+    inp = I.make_backward_inputs(wb)
+    d = {k: to_dev(inp[k]) for k in ("v", "delta", "g_w", "g_r", "rho", "theta", "c", "dy", "state_in", "dstate_out",
+                                     "zl")}
+    call = essh.PrefillBackward(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"], d["dy"], K_T=5,
+                                state_in=d["state_in"], dstate_out=d["dstate_out"], zl=d["zl"])
+
+    def bwd():
+        for t in call.grads.values():
+            if t is not None:
+                t.zero_()
+        call.run()
+        return list(call.grads.values())
+    log("backward: 50 identical calls")
+    assert not _repeat(bwd, 50), "backward calls differ"
