@@ -1003,7 +1003,6 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     auto bv_f32 = [&](const float4& b4, uint2 vf) __attribute__((always_inline)) -> f32x4_t {
         return f32x4_t{b4.x * lo_f32(vf.x), b4.y * hi_f32(vf.x), b4.z * lo_f32(vf.y), b4.w * hi_f32(vf.y)};
     };
-    const uint2 zero2 = make_uint2(0u, 0u);
 
     // One sub-block: optional outputs, then the state update; tr accumulates the
     // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
