@@ -12,14 +12,17 @@ constexpr int SCAN_PER = 16;
 // Entering states of the segments of every sequence from the segment
 // aggregates: E_1 = S_0 (segment 0's aggregate starts from state_in) and
 // E_{s+1} = Lambda_s E_s + S_s, the composition of Eq. 6's affine maps.  One
-// workgroup per (sequence, mode); thread (p, grp) composes the aggregates of
-// segments [16 grp, 16 grp + 16) for value column p, the groups' compositions
-// are exchanged through LDS, and each group then writes its entering states.
-__global__ void __launch_bounds__(1024) seg_scan_kernel(ScanPlan plan, int m, int P) {
+// workgroup per (sequence, mode, PC value columns); thread (p, grp) composes the
+// aggregates of segments [16 grp, 16 grp + 16) for value column p, the groups'
+// compositions are exchanged through LDS, and each group then writes its entering
+// states.  Sixteen columns per workgroup spread the launch over more CUs than one
+// workgroup per (sequence, mode) would.
+__global__ void __launch_bounds__(1024) seg_scan_kernel(ScanPlan plan, int m, int P, int PC) {
     __shared__ float4 comp[1024];
     const int ROWS = 2 * m;
     const int seq = blockIdx.x / m, j = blockIdx.x - seq * m;
-    const int p = threadIdx.x % P, grp = threadIdx.x / P;
+    const int pl = threadIdx.x % PC, grp = threadIdx.x / PC;
+    const int p = blockIdx.y * PC + pl;
     const int nag = plan.nseg - 1;
     const int s0 = grp * SCAN_PER;
     const size_t slot = (size_t)seq * plan.nseg;
@@ -54,7 +57,7 @@ __global__ void __launch_bounds__(1024) seg_scan_kernel(ScanPlan plan, int m, in
     __syncthreads();
     float hr = 0.f, hi = 0.f;   // value entering this group's first segment map
     for (int q = 0; q < grp; ++q) {
-        const float4 f = comp[q * P + p];
+        const float4 f = comp[q * PC + pl];
         const float nr = f.x * hr - f.y * hi + f.z, ni = f.x * hi + f.y * hr + f.w;
         hr = nr;
         hi = ni;
@@ -284,8 +287,9 @@ void bind_workspace(ScanPlan& p, void* ws, int m, int P) {
 
 hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s) {
     const int ngrp = (plan.nseg - 1 + SCAN_PER - 1) / SCAN_PER;
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(plan.nseq * m)), dim3((unsigned)(P * ngrp)), 0, s, plan, m,
-                       P);
+    const int PC = P < 16 ? P : 16;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(plan.nseq * m), (unsigned)(P / PC)),
+                       dim3((unsigned)(PC * ngrp)), 0, s, plan, m, P, PC);
     return hipGetLastError();
 }
 
