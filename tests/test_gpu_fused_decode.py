@@ -25,7 +25,10 @@ CASES = [("small_bf16", 2, 2, 4, 4, 32, 128, "bf16", (4, 2)),
          ("m1_p64", 2, 1, 2, 1, 64, 64, "bf16", (2, 1)),
          ("m8_p128_width_1000", 1, 2, 3, 8, 128, 1000, "bf16", (3,)),
          # the decode workload's layer shape (K=32, m=8, P=128, d = K P = 4096), two layers
-         ("decode_layer_shape", 2, 1, 32, 8, 128, 4096, "bf16", (32, 8))]
+         ("decode_layer_shape", 2, 1, 32, 8, 128, 4096, "bf16", (32, 8)),
+         # more than 256 channel workgroups (3 layers x 3 batch rows x 32 channels): the four-wave
+         # launch shape of the per-channel projections; at K_T = 8 (72 workgroups) the eight-wave one
+         ("many_channel_workgroups", 3, 3, 32, 8, 128, 4096, "bf16", (32, 8))]
 
 
 def log(msg):
