@@ -301,10 +301,11 @@ enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2, MODE_STREAM_PM = 3, MOD
 // need three workgroups' budget (168 VGPRs): four spilled 80-130 bytes per lane
 // and ran 370M-class tiers 15-25% slower, three runs them level with or faster
 // than the former four without the lo halves.  Streaming and per-mode launches
-// with up to four modes fit three workgroups in 168 VGPRs without spilling.  Measured on MI355X against the
-// unbounded two: the per-mode three-launch scan 16-17% faster (370M-class,
-// K_T = 6..24), the 128K-token three-launch scan 2-10% faster (K_T = 24..6).
-// Four spilled and was slower.
+// with up to four modes are held to three workgroups too.  The per-channel streaming
+// launches fit 168 VGPRs; the per-mode streaming launch with P = 64 and m = 4 spills
+// 88 bytes per lane there (since the carry readout's lo halves), and still runs the
+// 370M-class per-mode scan 6-11% faster than at two workgroups per CU (K_T = 24: 156
+// against 166 us).  Four spilled more and was slower.
 template <class C, int MODE>
 constexpr int min_workgroups_per_cu() {
     if (C::NW != 4 || C::M > 4) return 1;
