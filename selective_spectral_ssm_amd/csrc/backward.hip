@@ -59,6 +59,15 @@ constexpr int SB = 16;            // positions per sub-block
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+// eight fp32 values that are bf16 values (low 16 bits zero) as the eight bf16 of an MFMA
+// operand, element 0 first: the high halves, exactly
+__device__ __forceinline__ bf16x8 bf16_exact8(float4 a, float4 b) {
+    auto pk = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
+    const u32x4v w = {pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w)};
+    return __builtin_bit_cast(bf16x8, w);
+}
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
@@ -566,6 +575,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
                                                                                           BwdPlan pl) {
     constexpr int NT = NTC / 16, ROWS = 2 * M, KR = (ROWS + 3) / 4, LD = NTC + 4, KS = NTC / 4, LM = SB + 1;
     constexpr int CKN = M * NTC, CKE = (CKN + 63) / 64;   // complex state entries, per lane
+    constexpr bool BF16_S = sizeof(IO) == 2 && NTC % 32 == 0;   // S = dY V^T on the bf16 matrix cores
     __shared__ Tables<M> T;
     __shared__ float vt[SB * LD], dyt[SB * LD];   // v tile (then the dv tile) and dy tile
     // state entering the sub-block and adjoint arriving at its end, [row][column]; row 2m stays
@@ -751,25 +761,42 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) bw
         {
             const int ir = i < n ? n - 1 - i : SB - 1;   // reversed row of V for R (row 15 is zero when n < 16)
             const int ri = min(i, ROWS);                 // state row i (rows >= 2m: the zero row)
+            if constexpr (BF16_S) {
+                // dY and V hold bf16 values exactly, so S takes the bf16 matrix cores (32
+                // columns per v_mfma_f32_16x16x32_bf16, fp32 accumulation): lane (g, i) gives
+                // row i, columns c0 + 8 g .. c0 + 8 g + 7 of each
+#pragma unroll
+                for (int c0 = 0; c0 < NTC; c0 += 32) {
+                    const float* dr = dyt + i * LD + c0 + 8 * g;
+                    const float* vr = vt + i * LD + c0 + 8 * g;
+                    const bf16x8 da = bf16_exact8(*reinterpret_cast<const float4*>(dr),
+                                                  *reinterpret_cast<const float4*>(dr + 4));
+                    const bf16x8 vb = bf16_exact8(*reinterpret_cast<const float4*>(vr),
+                                                  *reinterpret_cast<const float4*>(vr + 4));
+                    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vb, S, 0, 0, 0);
+                }
+            }
             // four columns per 16-byte LDS read; one group at a time keeps few operands live
 #pragma unroll 1
             for (int k4 = 0; k4 < KS; k4 += 4) {
                 const int col = g * KS + k4;
                 const float4 d4 = *reinterpret_cast<const float4*>(dyt + i * LD + col);
-                const float4 v4 = *reinterpret_cast<const float4*>(vt + i * LD + col);
                 const float4 h4 = *reinterpret_cast<const float4*>(hs + ri * LD + col);
                 const float4 r4 = *reinterpret_cast<const float4*>(vt + ir * LD + col);
                 const float4 b4 = *reinterpret_cast<const float4*>(b1m + ri * LD + col);
-                S = mfma4(d4.x, v4.x, S);
+                if constexpr (!BF16_S) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(vt + i * LD + col);
+                    S = mfma4(d4.x, v4.x, S);
+                    S = mfma4(d4.y, v4.y, S);
+                    S = mfma4(d4.z, v4.z, S);
+                    S = mfma4(d4.w, v4.w, S);
+                }
                 Q = mfma4(h4.x, d4.x, Q);
                 R = mfma4(b4.x, r4.x, R);
-                S = mfma4(d4.y, v4.y, S);
                 Q = mfma4(h4.y, d4.y, Q);
                 R = mfma4(b4.y, r4.y, R);
-                S = mfma4(d4.z, v4.z, S);
                 Q = mfma4(h4.z, d4.z, Q);
                 R = mfma4(b4.z, r4.z, R);
-                S = mfma4(d4.w, v4.w, S);
                 Q = mfma4(h4.w, d4.w, Q);
                 R = mfma4(b4.w, r4.w, R);
             }
