@@ -177,6 +177,10 @@ struct __align__(16) Stage {
 // = fa[j][t] fb[j][s] for t, s in one sub-block; ftr[j][T] = e^{-(q_j(T1) - q_j(T0-1))},
 // T1 the sub-block's last valid position; fexact[T] = 1 where some mode's clock
 // span over the sub-block is too large to factor.
+// For the output operand as a rank-2m product (G = U W^T masked to s <= t, with
+// lambda^{t-s} = lambda^{t-T0} lambda^{T0-s}): ipw[e][j] = lambda_j^{-e}, e = 0..15;
+// zd[t] = sum_j g_r,j(t) g_w,j(t) a_j Re(c_j), the zero-lag term of the diagonal; lowrho = 1
+// where some rho_j^{-15} exceeds 2^40, and the sub-blocks then form G element by element.
 template <class C>
 struct __align__(16) StagePM {
     float q[C::M][C::LC];
@@ -186,6 +190,9 @@ struct __align__(16) StagePM {
     float fb[C::M][C::LC];
     float ftr[C::M][C::NSB];
     int fexact[C::NSB];
+    float2 ipw[16][C::M];
+    float zd[C::LC];
+    int lowrho;
 };
 
 // v tile of a staged chunk: [P/16][LC][16] bf16; y is staged in place.
@@ -596,6 +603,24 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         sm.psi[tau] = s;
     }
     lds_barrier();
+    if constexpr (PM) {
+        for (int idx = tid; idx < 16 * M; idx += C::THREADS) {
+            const int e = idx / M, j = idx - e * M;
+            const float4 mt = sm.mtab[j];
+            const float mag = e == 0 ? 1.f : exp2f(-(float)e * log2f(mt.x));
+            float sn, cs;
+            sincosf(-mt.y * (float)e, &sn, &cs);
+            spm.ipw[e][j] = make_float2(mag * cs, mag * sn);
+        }
+        if (tid == 0) {
+            int f = 0;
+#pragma unroll
+            for (int j = 0; j < M; ++j)
+                if (!(-15.f * log2f(sm.mtab[j].x) <= 40.f)) f = 1;   // also for rho <= 0 or NaN
+            spm.lowrho = f;
+        }
+        lds_barrier();
+    }
 
     // ---- per-lane constant MFMA operands ------------------------------------------------
     // Output product of target sub-block a of a block (B operands; lane (g, col)
@@ -944,6 +969,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 }
                 spm.fexact[i] = ex;
             }
+            for (int t = tid; t < LC; t += C::THREADS) {
+                float z = 0.f;
+#pragma unroll
+                for (int j = 0; j < M; ++j) z += spm.gr[j][t] * spm.gw[j][t] * sm.mza[j] * sm.mtab[j].z;
+                spm.zd[t] = z;
+            }
             __syncthreads();
         }
     };
@@ -1071,15 +1102,45 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 if (out) {
                     const int t = T0 + col;
                     float gv[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (!spm.lowrho) {
+                        // G^T = W U^T on the fp32 matrix cores, rank 2m: U[t][2j, 2j+1] =
+                        // fa_j(t) {Re, -Im}(c_j lambda_j^{t-T0}), W[s][2j, 2j+1] = fb_j(s)
+                        // {Re, Im}(lambda_j^{T0-s}); lane (g, col) gives row col of each, columns
+                        // 4 kb + g, and gets G[t][s = T0 + 4g + e] in element e.  Row T0 of U
+                        // takes c_j itself (the lag-0 coefficient without the zero-lag term);
+                        // the diagonal then loses zd.
+                        f32x4_t gd = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < M; ++j) {
-                        const float fat = spm.fa[j][t];
-                        const float4 fb4 = *reinterpret_cast<const float4*>(&spm.fb[j][T0 + 4 * g]);
-                        const float fbs[4] = {fb4.x, fb4.y, fb4.z, fb4.w};
+                        for (int kb = 0; kb < (2 * M + 3) / 4; ++kb) {
+                            const int k = 4 * kb + g, j = k >> 1;
+                            float u = 0.f, w = 0.f;
+                            if (j < M) {
+                                const int jj = j < M ? j : 0;
+                                const float4 mt = sm.mtab[jj];
+                                const float2 cp = col == 0 ? make_float2(mt.z, mt.w) : sm.cpw[col][jj];
+                                const float2 ip = spm.ipw[col][jj];
+                                u = spm.fa[jj][t] * ((k & 1) ? -cp.y : cp.x);
+                                w = spm.fb[jj][t] * ((k & 1) ? ip.y : ip.x);
+                            }
+                            gd = __builtin_amdgcn_mfma_f32_16x16x4f32(w, u, gd, 0, 0, 0);
+                        }
+                        const float zdt = spm.zd[t];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int sl = 4 * g + e;
-                            if (sl <= col) gv[e] += fat * fbs[e] * sm.cpw[col - sl][j].x;
+                            gv[e] = sl < col ? gd[e] : sl == col ? gd[e] - zdt : 0.f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < M; ++j) {
+                            const float fat = spm.fa[j][t];
+                            const float4 fb4 = *reinterpret_cast<const float4*>(&spm.fb[j][T0 + 4 * g]);
+                            const float fbs[4] = {fb4.x, fb4.y, fb4.z, fb4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int sl = 4 * g + e;
+                                if (sl <= col) gv[e] += fat * fbs[e] * sm.cpw[col - sl][j].x;
+                            }
                         }
                     }
 #pragma unroll

@@ -262,6 +262,25 @@ def test_prefill_per_mode_chunked(name, widx, over, K_T, Lc):
     check_prefill(name + "_zero_lag", inp, K_T, Lc, zl=zl)
 
 
+def test_prefill_per_mode_small_rho():
+    """Per-mode chunks whose magnitudes rho reach down to 0.05 (Eq. 5 allows any rho in (0,1)):
+    channels whose rho^-15 stays within 2^40 build the output operand as a rank-2m product of
+    lambda^(t-T0) and lambda^(T0-s), the rest element by element; both must give the oracle's y."""
+    w = I.workload(1, B=2, L=230, K=6, rho_lo=0.05, rho_hi=0.6)
+    inp = I.make_prefill_inputs(w, per_mode=True)
+    rho = inp["rho"]
+    rho[0, :] = 0.16              # every mode just inside the product's range (0.16^-15 ~ 2^39.7)
+    rho[1, :] = 0.5
+    rho[1, 2] = 0.15              # one mode just outside it: the whole channel takes the other form
+    rho[2, :] = 0.9
+    rng = np.random.default_rng(37)
+    s0 = rng.normal(0, 1.0, size=(w.B, w.K, w.m, 2, w.P)).astype(np.float32)
+    zl = rng.uniform(0.0, 1.0, size=(w.K, w.m)).astype(np.float32)
+    for Lc in (64, 128):
+        check_prefill(f"pm_small_rho_lc{Lc}", inp, w.K, Lc, state_in=s0)
+        check_prefill(f"pm_small_rho_zero_lag_lc{Lc}", inp, w.K, Lc, zl=zl)
+
+
 @pytest.mark.parametrize("per_mode", [False, True], ids=["per_channel", "per_mode"])
 def test_prefill_large_clock_spans(per_mode):
     """Clock spans too large to factor (Eq. 6's decay e^{-sum delta} far below fp32 range over a
