@@ -193,6 +193,13 @@ struct __align__(16) StagePM {
     float2 ipw[16][C::M];
     float zd[C::LC];
     int lowrho;
+    // The sub-blocks' operands in MFMA lane order ([G ; C hi], [C lo ; C hi], W hi and lo),
+    // formed once per chunk by one wave each and read by every wave; chunks of at most four
+    // sub-blocks (a longer chunk forms them in each wave, as LDS is short there).
+    static constexpr int NOP = C::NSB <= 4 ? C::NSB : 1;
+    bf16x8_t opg[NOP][64];
+    bf16x8_t opgx[NOP][64];
+    bf16x8_t opw[NOP][64];
 };
 
 // v tile of a staged chunk: [P/16][LC][16] bf16; y is staged in place.
@@ -310,11 +317,14 @@ enum { MODE_STREAM = 0, MODE_LOOKBACK = 1, MODE_AGG = 2, MODE_STREAM_PM = 3, MOD
 // than the former four without the lo halves.  Streaming and per-mode launches
 // with up to four modes are held to three workgroups too.  The per-channel streaming
 // launches fit 168 VGPRs; the per-mode streaming launch with P = 64 and m = 4 spills
-// 88 bytes per lane there (since the carry readout's lo halves), and still runs the
-// 370M-class per-mode scan 6-11% faster than at two workgroups per CU (K_T = 24: 156
-// against 166 us).  Four spilled more and was slower.
+// about 120 bytes per lane there (since the carry readout's lo halves and the output
+// operand's MFMA form), and ran the 370M-class per-mode scan 6-11% faster than at two
+// workgroups per CU when measured (K_T = 24: 156 against 166 us).  Four spilled more and
+// was slower.  The per-mode streaming launch with m = 8 is held to two workgroups per CU:
+// unbounded it took 259 registers and ran one wave per SIMD.
 template <class C, int MODE>
 constexpr int min_workgroups_per_cu() {
+    if (C::NW == 4 && C::M > 4 && MODE == MODE_STREAM_PM) return 2;
     if (C::NW != 4 || C::M > 4) return 1;
     if (MODE == MODE_LOOKBACK) return 3;
     if (MODE == MODE_STREAM || MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM) return 3;
@@ -329,6 +339,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     constexpr bool SEG = MODE == MODE_LOOKBACK;
     constexpr bool AGG = MODE == MODE_AGG || MODE == MODE_AGG_PM;
     constexpr bool PM = MODE == MODE_STREAM_PM || MODE == MODE_AGG_PM;   // per-mode controls
+    constexpr bool PM_OPS = PM && C::NSB <= 4;   // per-mode operands formed per chunk, in LDS
     constexpr int NB = C::NB, BLK = C::BLK;   // sub-blocks per arithmetic block
     // The staged chunks are an LDS object of their own, so that accesses to
     // the tables in sm are not ordered behind the asynchronous tile copies.
@@ -1036,68 +1047,20 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         return f32x4_t{b4.x * lo_f32(vf.x), b4.y * hi_f32(vf.x), b4.z * lo_f32(vf.y), b4.w * hi_f32(vf.y)};
     };
 
-    // One sub-block: optional outputs, then the state update; tr accumulates the
-    // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
-    auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4], const bf16x8_t& al,
-                        const float (&l16)[4]) __attribute__((always_inline)) {
-        const int T0 = T * 16;
-        const float2 bk = sgp->blk[T];
-        uint2 vfr[NTW];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) vfr[nt] = load_vfrag(T, nt);
-        float lam[4];   // Lambda_T for modes 2g, 2g+1
-        if (bk.y == 0.f) {
-            // factored path: scale v by b(s), constant operands.  b(s) v(s) is
-            // split into a bf16 hi half, which feeds the output product, and a bf16
-            // lo half; the state product takes both halves against the hi and lo
-            // halves of the lambda powers, and the carry term takes the hi and lo
-            // halves of the state, so both state-side contractions keep fp32-class
-            // precision.
-            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
-            uint2 bv[NTW], bvl[NTW];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const f32x4_t f = bv_f32(b4, vfr[nt]);
-                bv[nt] = hi4(f);
-                bvl[nt] = lo4(f, bv[nt]);
-            }
-            if (out) {
-                const float sc = sgp->ag[T0 + col];
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const uint2 hh = hi4(st[nt]);
-                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bf16x8_of(bv[nt], hh), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), yDx[0], acc, 0,
-                                                                  0, 0);
-                    stage_y(T, nt, acc, sc);
-                }
-            }
-            const float at = bk.x;
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
-                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bvl[nt], bvl[nt]), mv, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const float lr = l16[i], li = l16[i + 1];
-                    const float hr = st[nt][i], hi = st[nt][i + 1];
-                    st[nt][i] = at * (lr * hr - li * hi + mv[i]);
-                    st[nt][i + 1] = at * (li * hr + lr * hi + mv[i + 1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lam[i] = at * l16[i];
-        } else if constexpr (PM) {
-            // per-mode controls: operands per element and mode, the read gate
-            // inside the sum over modes
-            //   G[t][s]  = sum_j g_r,j(t) e^{-(qj(t)-qj(s))} g_w,j(s) Re(c_j lambda_j^{t-s})  (s <= t)
-            //   C[t][jr] = g_r,j(t) e^{-(qj(t)-qj(T0-1))} {Re, -Im}(c_j lambda_j^{t-T0+1})
-            //   W[jr][s] = {Re, Im}(lambda_j^{T1-s}) e^{-(qj(T1)-qj(s))} g_w,j(s)
-            // from the staged factors fa, fb, ftr (products, no exponentials), or,
-            // where a mode's clock span is too large to factor, from the clock sums.
-            const int T1 = min(T0 + 15, n - 1);
+    // Per-mode operands of sub-block T, per element and mode, with the read gate inside the
+    // sum over modes:
+    //   G[t][s]  = sum_j g_r,j(t) e^{-(qj(t)-qj(s))} g_w,j(s) Re(c_j lambda_j^{t-s})  (s <= t)
+    //   C[t][jr] = g_r,j(t) e^{-(qj(t)-qj(T0-1))} {Re, -Im}(c_j lambda_j^{t-T0+1})
+    //   W[jr][s] = {Re, Im}(lambda_j^{T1-s}) e^{-(qj(T1)-qj(s))} g_w,j(s)
+    // from the staged factors fa, fb, ftr (products, no exponentials), or, where a mode's
+    // clock span is too large to factor, from the clock sums.  With out: bx = [G ; C hi] and
+    // bxx = [C lo ; C hi] (the carry coefficients in bf16 hi and lo halves, since mode terms
+    // may cancel).  wf = W in hi and lo halves.
+    auto pm_operands = [&](int T, int n, bool out, bf16x8_t& bx, bf16x8_t& bxx,
+                           bf16x8_t& wf) __attribute__((always_inline)) {
+        if constexpr (PM) {
+            const int T0 = T * 16, T1 = min(T0 + 15, n - 1);
+            float wv[4];
             if (spm.fexact[T] == 0) {
                 if (out) {
                     const int t = T0 + col;
@@ -1152,64 +1115,23 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             av[i] = spm.fa[jj][t] * ((row & 1) ? -cp.y : cp.x);
                         }
                     }
-                    // carry coefficients in bf16 hi and lo halves (mode terms may cancel)
                     const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
                     const uint2 ah4 = hi4(af);
-                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
-                    const bf16x8_t bxx = bf16x8_of(lo4(af, ah4), ah4);
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) {
-                        const uint2 hh = hi4(st[nt]);
-                        f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0,
-                                                                      0, 0);
-                        stage_y(T, nt, acc, 1.f);
-                    }
+                    bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                    bxx = bf16x8_of(lo4(af, ah4), ah4);
                 }
-                float wv[4];
-                {
-                    const int jr = col >> 1;
-                    const int jj = jr < M ? jr : 0;
-                    const float trj = spm.ftr[jj][T];
+                const int jr = col >> 1;
+                const int jj = jr < M ? jr : 0;
+                const float trj = spm.ftr[jj][T];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s2 = T0 + 4 * g + e;
-                        float val = 0.f;
-                        if (jr < M && s2 <= T1) {
-                            const float2 pw = sm.pw[T1 - s2][jj];
-                            val = ((col & 1) ? pw.y : pw.x) * spm.fb[jj][s2] * trj;
-                        }
-                        wv[e] = val;
+                for (int e = 0; e < 4; ++e) {
+                    const int s2 = T0 + 4 * g + e;
+                    float val = 0.f;
+                    if (jr < M && s2 <= T1) {
+                        const float2 pw = sm.pw[T1 - s2][jj];
+                        val = ((col & 1) ? pw.y : pw.x) * spm.fb[jj][s2] * trj;
                     }
-                }
-                const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
-                const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
-                                              make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
-                                                         pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int j = 2 * g + hh;
-                    float2 pn = make_float2(0.f, 0.f);
-                    float at = 0.f;
-                    if (j < M) {
-                        const int jj = j < M ? j : 0;
-                        at = spm.ftr[jj][T];
-                        pn = sm.pw[T1 - T0 + 1][jj];
-                    }
-                    lam[2 * hh] = at * pn.x;
-                    lam[2 * hh + 1] = at * pn.y;
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    f32x4_t d;
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const float hr = st[nt][i], hi = st[nt][i + 1];
-                        d[i] = lam[i] * hr - lam[i + 1] * hi;
-                        d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
-                    }
-                    st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
+                    wv[e] = val;
                 }
             } else {
                 if (out) {
@@ -1239,66 +1161,136 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             av[i] = ea * ((row & 1) ? -cp.y : cp.x);
                         }
                     }
-                    // carry coefficients in bf16 hi and lo halves (mode terms may cancel)
                     const f32x4_t af = f32x4_t{av[0], av[1], av[2], av[3]};
                     const uint2 ah4 = hi4(af);
-                    const bf16x8_t bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
-                    const bf16x8_t bxx = bf16x8_of(lo4(af, ah4), ah4);
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) {
-                        const uint2 hh = hi4(st[nt]);
-                        f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0,
-                                                                      0, 0);
-                        stage_y(T, nt, acc, 1.f);
-                    }
+                    bx = bf16x8_of(make_uint2(pk_bf16(gv[0], gv[1]), pk_bf16(gv[2], gv[3])), ah4);
+                    bxx = bf16x8_of(lo4(af, ah4), ah4);
                 }
-                float wv[4];
-                {
-                    const int jr = col >> 1;
-                    const int jj = jr < M ? jr : 0;
-                    const float qe = spm.q[jj][T1];
+                const int jr = col >> 1;
+                const int jj = jr < M ? jr : 0;
+                const float qe = spm.q[jj][T1];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s2 = T0 + 4 * g + e;
-                        float val = 0.f;
-                        if (jr < M && s2 <= T1) {
-                            const float2 pw = sm.pw[T1 - s2][jj];
-                            val = ((col & 1) ? pw.y : pw.x) * exp2f(spm.q[jj][s2] - qe) * spm.gw[jj][s2];
-                        }
-                        wv[e] = val;
+                for (int e = 0; e < 4; ++e) {
+                    const int s2 = T0 + 4 * g + e;
+                    float val = 0.f;
+                    if (jr < M && s2 <= T1) {
+                        const float2 pw = sm.pw[T1 - s2][jj];
+                        val = ((col & 1) ? pw.y : pw.x) * exp2f(spm.q[jj][s2] - qe) * spm.gw[jj][s2];
                     }
+                    wv[e] = val;
                 }
-                const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
-                const bf16x8_t wf = bf16x8_of(make_uint2(w01, w23),
-                                              make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
-                                                         pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
+            }
+            const uint32_t w01 = pk_bf16(wv[0], wv[1]), w23 = pk_bf16(wv[2], wv[3]);
+            wf = bf16x8_of(make_uint2(w01, w23), make_uint2(pk_bf16(wv[0] - lo_f32(w01), wv[1] - hi_f32(w01)),
+                                                           pk_bf16(wv[2] - lo_f32(w23), wv[3] - hi_f32(w23))));
+        }
+    };
+
+    // One sub-block: optional outputs, then the state update; tr accumulates the
+    // sub-block transfers (modes 2g, 2g+1) for the segment aggregate.
+    auto subblock = [&](f32x4_t (&st)[NTW], int T, int n, bool out, float (&tr)[4], const bf16x8_t& al,
+                        const float (&l16)[4]) __attribute__((always_inline)) {
+        const int T0 = T * 16;
+        const float2 bk = sgp->blk[T];
+        uint2 vfr[NTW];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int j = 2 * g + hh;
-                    float2 pn = make_float2(0.f, 0.f);
-                    float at = 0.f;
-                    if (j < M) {
-                        const int jj = j < M ? j : 0;
-                        const float qp = T0 > 0 ? spm.q[jj][T0 - 1] : 0.f;
-                        at = exp2f(qp - spm.q[jj][T1]);
-                        pn = sm.pw[T1 - T0 + 1][jj];
-                    }
-                    lam[2 * hh] = at * pn.x;
-                    lam[2 * hh + 1] = at * pn.y;
-                }
+        for (int nt = 0; nt < NTW; ++nt) vfr[nt] = load_vfrag(T, nt);
+        float lam[4];   // Lambda_T for modes 2g, 2g+1
+        if (bk.y == 0.f) {
+            // factored path: scale v by b(s), constant operands.  b(s) v(s) is
+            // split into a bf16 hi half, which feeds the output product, and a bf16
+            // lo half; the state product takes both halves against the hi and lo
+            // halves of the lambda powers, and the carry term takes the hi and lo
+            // halves of the state, so both state-side contractions keep fp32-class
+            // precision.
+            const float4 b4 = *reinterpret_cast<const float4*>(&sgp->bq[T0 + 4 * g]);
+            uint2 bv[NTW], bvl[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const f32x4_t f = bv_f32(b4, vfr[nt]);
+                bv[nt] = hi4(f);
+                bvl[nt] = lo4(f, bv[nt]);
+            }
+            if (out) {
+                const float sc = sgp->ag[T0 + col];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    f32x4_t d;
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const float hr = st[nt][i], hi = st[nt][i + 1];
-                        d[i] = lam[i] * hr - lam[i + 1] * hi;
-                        d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
-                    }
-                    st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
+                    const uint2 hh = hi4(st[nt]);
+                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(bv[nt], hh), yD[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), yDx[0], acc, 0,
+                                                                  0, 0);
+                    stage_y(T, nt, acc, sc);
                 }
+            }
+            const float at = bk.x;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4_t mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bv[nt], bv[nt]),
+                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                mv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf16x8_of(bvl[nt], bvl[nt]), mv, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float lr = l16[i], li = l16[i + 1];
+                    const float hr = st[nt][i], hi = st[nt][i + 1];
+                    st[nt][i] = at * (lr * hr - li * hi + mv[i]);
+                    st[nt][i + 1] = at * (li * hr + lr * hi + mv[i + 1]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[i] = at * l16[i];
+        } else if constexpr (PM) {
+            // per-mode controls: the operands of pm_operands, formed for the whole chunk before
+            // its sub-blocks where they are held in LDS, else here
+            const int T1 = min(T0 + 15, n - 1);
+            bf16x8_t bx, bxx, wf;
+            if constexpr (PM_OPS) {
+                if (out) {
+                    bx = spm.opg[T][lane];
+                    bxx = spm.opgx[T][lane];
+                }
+                wf = spm.opw[T][lane];
+            } else {
+                pm_operands(T, n, out, bx, bxx, wf);
+            }
+            if (out) {
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const uint2 hh = hi4(st[nt]);
+                    f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bf16x8_of(vfr[nt], hh), bx, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x8_of(hh, lo4(st[nt], hh)), bxx, acc, 0, 0,
+                                                                  0);
+                    stage_y(T, nt, acc, 1.f);
+                }
+            }
+            // Lambda_T of modes 2g, 2g+1: the clock factor of the whole sub-block (staged, or
+            // from the clock sums where the span is too large to factor) and lambda^len
+            const bool fac = spm.fexact[T] == 0;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = 2 * g + hh;
+                float2 pn = make_float2(0.f, 0.f);
+                float at = 0.f;
+                if (j < M) {
+                    const int jj = j < M ? j : 0;
+                    const float qp = T0 > 0 ? spm.q[jj][T0 - 1] : 0.f;
+                    at = fac ? spm.ftr[jj][T] : exp2f(qp - spm.q[jj][T1]);
+                    pn = sm.pw[T1 - T0 + 1][jj];
+                }
+                lam[2 * hh] = at * pn.x;
+                lam[2 * hh + 1] = at * pn.y;
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4_t d;
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float hr = st[nt][i], hi = st[nt][i + 1];
+                    d[i] = lam[i] * hr - lam[i + 1] * hi;
+                    d[i + 1] = lam[i + 1] * hr + lam[i] * hi;
+                }
+                st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, bf16x8_of(vfr[nt], vfr[nt]), d, 0, 0, 0);
             }
         } else {
             // exact path (ragged sub-block, or a clock span too large to factor):
@@ -1508,6 +1500,19 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // All positions of the staged chunk (n valid): whole blocks on the block
     // path, the others (ragged, or a clock span too large) sub-block by sub-block.
     auto chunk_pass = [&](f32x4_t (&st)[NTW], int n, bool out, float (&tr)[4]) __attribute__((always_inline)) {
+        if constexpr (PM_OPS) {
+            // every sub-block's operands, wave w forming those of sub-blocks w, w + NW, ...
+            for (int T = wave; T * 16 < n; T += C::NW) {
+                bf16x8_t bx, bxx, wf;
+                pm_operands(T, n, out, bx, bxx, wf);
+                if (out) {
+                    spm.opg[T][lane] = bx;
+                    spm.opgx[T][lane] = bxx;
+                }
+                spm.opw[T][lane] = wf;
+            }
+            lds_barrier();
+        }
         for (int Bi = 0; Bi * BLK < n; ++Bi) {
             if (sgp->blkB[Bi].w == 0.f) {
                 block_fast(st, Bi, out, false, tr);
