@@ -179,8 +179,8 @@ struct __align__(16) Stage {
 // span over the sub-block is too large to factor.
 // For the output operand as a rank-2m product (G = U W^T masked to s <= t, with
 // lambda^{t-s} = lambda^{t-T0} lambda^{T0-s}): ipw[e][j] = lambda_j^{-e}, e = 0..15;
-// zd[t] = sum_j g_r,j(t) g_w,j(t) a_j Re(c_j), the zero-lag term of the diagonal; lowrho = 1
-// where some rho_j^{-15} exceeds 2^40, and the sub-blocks then form G element by element.
+// lowrho = 1 where some rho_j^{-15} exceeds 2^40, and the sub-blocks then form G element
+// by element.
 template <class C>
 struct __align__(16) StagePM {
     float q[C::M][C::LC];
@@ -191,7 +191,6 @@ struct __align__(16) StagePM {
     float ftr[C::M][C::NSB];
     int fexact[C::NSB];
     float2 ipw[16][C::M];
-    float zd[C::LC];
     int lowrho;
     // The sub-blocks' operands in MFMA lane order ([G ; C hi], [C lo ; C hi], W hi and lo),
     // formed once per chunk by one wave each and read by every wave; chunks of at most four
@@ -906,6 +905,21 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         }
     };
 
+    // Per-mode controls: 1 where some mode's clock span over sub-block T (n valid positions in
+    // the chunk, clock sums staged) is too large for the factored operands.
+    auto pm_exact = [&](int T, int n) __attribute__((always_inline)) -> int {
+        int ex = 0;
+        if constexpr (PM) {
+            const int T0 = 16 * T, T1 = min(T0 + 15, n - 1);
+            if (T0 < n) {
+#pragma unroll
+                for (int j = 0; j < M; ++j)
+                    if (spm.q[j][T1] - (T0 > 0 ? spm.q[j][T0 - 1] : 0.f) > SPAN2_FAST_MAX) ex = 1;
+            }
+        }
+        return ex;
+    };
+
     // Register path: v tile and controls of the loaded chunk -> LDS, then the
     // loads of chunk `next` (if >= 0) are issued so that they overlap this
     // chunk's arithmetic.  Starts and ends with a barrier.
@@ -937,7 +951,8 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         if (next >= 0) load_chunk(rg, next);
         __syncthreads();
         if constexpr (PM) {
-            // clock sums of each mode over the chunk (wave w: modes w, w + NW, ...)
+            // clock sums of each mode over the chunk and, from them, the factors of the clock
+            // referenced to each sub-block's start (wave w: modes w, w + NW, ...)
             for (int j = wave; j < M; j += C::NW) {
                 float loc[C::CPL];
                 float run = 0.f;
@@ -954,37 +969,31 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     if (lane >= off) incl += o;
                 }
                 const float excl = incl - run;
+                float qv[C::CPL];
+#pragma unroll
+                for (int u = 0; u < C::CPL; ++u) qv[u] = (excl + loc[u]) * LOG2E;
+                // the clock sum just before this lane's sub-block (CPL divides 16, so a lane's
+                // positions share one sub-block and position T0 - 1 is a lane's last)
+                const int T0 = (lane * C::CPL) & ~15;
+                const float qb = __shfl(qv[C::CPL - 1], T0 > 0 ? T0 / C::CPL - 1 : 0);
+                const float qp = T0 > 0 ? qb : 0.f;
 #pragma unroll
                 for (int u = 0; u < C::CPL; ++u) {
-                    const int idx = lane * C::CPL + u;
-                    if (idx < LC) spm.q[j][idx] = (excl + loc[u]) * LOG2E;
+                    const int t = lane * C::CPL + u;
+                    if (t < LC) {
+                        spm.q[j][t] = qv[u];
+                        const float d = qv[u] - qp;   // >= 0 (log2 units)
+                        spm.fa[j][t] = exp2f(-d) * spm.gr[j][t];
+                        spm.fb[j][t] = t < n ? exp2f(d) * spm.gw[j][t] : 0.f;
+                        if (t == min(T0 + 15, n - 1)) spm.ftr[j][t >> 4] = exp2f(-d);
+                    }
                 }
             }
-            __syncthreads();
-            // factors of the clock referenced to each sub-block's start, per mode
-            for (int e = tid; e < M * LC; e += C::THREADS) {
-                const int j = e / LC, t = e - j * LC;
-                const int T0 = t & ~15;
-                const float d = spm.q[j][t] - (T0 > 0 ? spm.q[j][T0 - 1] : 0.f);   // >= 0 (log2 units)
-                spm.fa[j][t] = exp2f(-d) * spm.gr[j][t];
-                spm.fb[j][t] = t < n ? exp2f(d) * spm.gw[j][t] : 0.f;
-                if (t == min(T0 + 15, n - 1)) spm.ftr[j][t >> 4] = exp2f(-d);
-            }
-            for (int i = tid; i < C::NSB; i += C::THREADS) {
-                const int T0 = 16 * i, T1 = min(T0 + 15, n - 1);
-                int ex = 0;
-                if (T0 < n) {
-#pragma unroll
-                    for (int j = 0; j < M; ++j)
-                        if (spm.q[j][T1] - (T0 > 0 ? spm.q[j][T0 - 1] : 0.f) > SPAN2_FAST_MAX) ex = 1;
-                }
-                spm.fexact[i] = ex;
-            }
-            for (int t = tid; t < LC; t += C::THREADS) {
-                float z = 0.f;
-#pragma unroll
-                for (int j = 0; j < M; ++j) z += spm.gr[j][t] * spm.gw[j][t] * sm.mza[j] * sm.mtab[j].z;
-                spm.zd[t] = z;
+            if constexpr (!PM_OPS) {
+                // sub-blocks whose clock span is too large to factor (with operands formed per
+                // chunk, the wave forming a sub-block's operands decides this)
+                __syncthreads();
+                for (int i = tid; i < C::NSB; i += C::THREADS) spm.fexact[i] = pm_exact(i, n);
             }
             __syncthreads();
         }
@@ -1056,12 +1065,12 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // clock span is too large to factor, from the clock sums.  With out: bx = [G ; C hi] and
     // bxx = [C lo ; C hi] (the carry coefficients in bf16 hi and lo halves, since mode terms
     // may cancel).  wf = W in hi and lo halves.
-    auto pm_operands = [&](int T, int n, bool out, bf16x8_t& bx, bf16x8_t& bxx,
+    auto pm_operands = [&](int T, int n, bool out, bool fac, bf16x8_t& bx, bf16x8_t& bxx,
                            bf16x8_t& wf) __attribute__((always_inline)) {
         if constexpr (PM) {
             const int T0 = T * 16, T1 = min(T0 + 15, n - 1);
             float wv[4];
-            if (spm.fexact[T] == 0) {
+            if (fac) {
                 if (out) {
                     const int t = T0 + col;
                     float gv[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1087,7 +1096,9 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                             }
                             gd = __builtin_amdgcn_mfma_f32_16x16x4f32(w, u, gd, 0, 0, 0);
                         }
-                        const float zdt = spm.zd[t];
+                        float zdt = 0.f;   // the zero-lag term of the diagonal
+#pragma unroll
+                        for (int j = 0; j < M; ++j) zdt += spm.gr[j][t] * spm.gw[j][t] * sm.mza[j] * sm.mtab[j].z;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int sl = 4 * g + e;
@@ -1251,7 +1262,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                 }
                 wf = spm.opw[T][lane];
             } else {
-                pm_operands(T, n, out, bx, bxx, wf);
+                pm_operands(T, n, out, spm.fexact[T] == 0, bx, bxx, wf);
             }
             if (out) {
 #pragma unroll
@@ -1503,8 +1514,10 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         if constexpr (PM_OPS) {
             // every sub-block's operands, wave w forming those of sub-blocks w, w + NW, ...
             for (int T = wave; T * 16 < n; T += C::NW) {
+                const int ex = pm_exact(T, n);
+                if (lane == 0) spm.fexact[T] = ex;
                 bf16x8_t bx, bxx, wf;
-                pm_operands(T, n, out, bx, bxx, wf);
+                pm_operands(T, n, out, ex == 0, bx, bxx, wf);
                 if (out) {
                     spm.opg[T][lane] = bx;
                     spm.opgx[T][lane] = bxx;
