@@ -16,7 +16,8 @@ constexpr int SCAN_PER = 16;
 // aggregates of segments [16 grp, 16 grp + 16) for value column p, the groups'
 // compositions are exchanged through LDS, and each group then writes its entering
 // states.  Sixteen columns per workgroup spread the launch over more CUs than one
-// workgroup per (sequence, mode) would.
+// workgroup per (sequence, mode) would; with few segments per sequence (fewer than 64
+// threads at 16 columns) a workgroup takes more columns, up to P.
 __global__ void __launch_bounds__(1024) seg_scan_kernel(ScanPlan plan, int m, int P, int PC) {
     __shared__ float4 comp[1024];
     const int ROWS = 2 * m;
@@ -287,7 +288,11 @@ void bind_workspace(ScanPlan& p, void* ws, int m, int P) {
 
 hipError_t launch_seg_scan(const ScanPlan& plan, int m, int P, hipStream_t s) {
     const int ngrp = (plan.nseg - 1 + SCAN_PER - 1) / SCAN_PER;
-    const int PC = P < 16 ? P : 16;
+    // value columns per workgroup: 16, or more (a power of two dividing P) until the
+    // workgroup fills a wave, so that few segments per sequence do not launch thousands of
+    // quarter-wave workgroups
+    int PC = P < 16 ? P : 16;
+    while (2 * PC <= P && PC * ngrp < 64) PC *= 2;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(plan.nseq * m), (unsigned)(P / PC)),
                        dim3((unsigned)(PC * ngrp)), 0, s, plan, m, P, PC);
     return hipGetLastError();
