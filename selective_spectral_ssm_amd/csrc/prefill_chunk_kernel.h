@@ -1559,8 +1559,11 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
     // staged y -> global by whole rows, non-temporally: each 128-byte line is
     // written by one instruction, so none is left dirty in L2 when the kernel
     // ends.  Needs every wave's y of the chunk staged (a barrier before).  Used
-    // with P <= 64 by the look-back launch and the streaming launch (measured
-    // faster there; with wider rows the read-back crosses too many tile blocks).
+    // with P <= 64 by the look-back launch and the streaming launches, per-channel
+    // and per-mode (measured faster there; with wider rows the read-back crosses
+    // too many tile blocks).  In the per-mode launch, whose address registers
+    // spill, the per-wave stores each waited for a reload and so for the store
+    // before it: whole rows took the 370M-class per-mode call from 120 to 116 us.
     auto store_y_rows = [&](int t0, int n) __attribute__((always_inline)) {
         constexpr int UPR = P / 8;                     // 16-byte units per row
         constexpr int RPW = 64 / UPR;                  // rows per wave instruction
@@ -1863,7 +1866,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             const int n = min(LC, L - t0);
             __builtin_amdgcn_s_waitcnt(WAIT_VMEM0);   // loads of chunk c, issued a chunk ago
             if (!AGG && yt0 >= 0) {
-                if constexpr (P <= 64 && MODE == MODE_STREAM) {
+                if constexpr (P <= 64 && (MODE == MODE_STREAM || MODE == MODE_STREAM_PM)) {
                     lds_barrier();   // every wave's y of chunk c-1 is staged
                     store_y_rows(yt0, yn);
                 } else {
@@ -1876,7 +1879,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
             yn = n;
         }
         if (!AGG && yt0 >= 0) {
-            if constexpr (P <= 64 && MODE == MODE_STREAM) {
+            if constexpr (P <= 64 && (MODE == MODE_STREAM || MODE == MODE_STREAM_PM)) {
                 lds_barrier();
                 store_y_rows(yt0, yn);
             } else {
