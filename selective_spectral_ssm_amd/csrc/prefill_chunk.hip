@@ -197,6 +197,25 @@ ScanPlan plan_chunked(int B, int L, int K_T, int m, int P, int Lc, int per_mode)
             const int max_seg = 1 + SCAN_PER * (1024 / P);
             const int min_chunks = (p.nchunks + max_seg - 1) / max_seg;
             seg_chunks = (int)(want > min_chunks ? want : min_chunks);
+            if (per_mode && P >= 64) {
+                // Per-mode controls with four-wave workgroups: the segment length that
+                // minimises rounds x chunks per segment, where a round is the workgroup slots
+                // of 256 CUs at three workgroups per CU (m <= 4) or two (m = 8); on a tie the
+                // longer segment, which leaves the aggregate launch less to do.  Measured on
+                // MI355X: the 370M-class per-mode call at K_T = 24 took 101 us with segments of
+                // 8 chunks (one round) against 114 with 4 (two rounds), the 1.5B-class at
+                // K_T = 8 110 against 137.5 with 3.
+                const long long slots = 256LL * (m <= 4 ? 3 : 2);
+                long long best = -1;
+                for (int c = min_chunks; c <= p.nchunks; ++c) {
+                    const long long wgs = (long long)p.nseq * ((p.nchunks + c - 1) / c);
+                    const long long cost = ((wgs + slots - 1) / slots) * c;
+                    if (best < 0 || cost <= best) {
+                        best = cost;
+                        seg_chunks = c;
+                    }
+                }
+            }
         } else {
             p.mode = SCAN_LOOKBACK;
             seg_chunks = resident_chunks(P, Lc);

@@ -471,6 +471,46 @@ def test_prefill_full_size_sampled(widx, K_T):
         assert es <= STATE_REGRESSION_BF16, f"state error {es:.3e} above its regression bound"
 
 
+# The per-mode control form (Eq. 5: clock and gates [B, L, K, m]) at the full sizes and tiers
+# bench.py times it, whose plans (segment lengths filling whole rounds of workgroups, whole
+# sequences at the 1.5B-class K_T = 32) no reduced shape reaches: sampled sequences against
+# the oracle, y and final state.
+FULL_PM = [(1, 24), (1, 12), (1, 6), (2, 8), (2, 32)]
+_FULL_PM_INPUTS = {}
+
+
+@pytest.mark.parametrize("widx,K_T", FULL_PM, ids=[f"{I.WORKLOADS[wi].name}_KT{kt}" for wi, kt in FULL_PM])
+def test_prefill_per_mode_full_size_sampled(widx, K_T):
+    import torch
+    essh = _essh()
+    if widx not in _FULL_PM_INPUTS:
+        _FULL_PM_INPUTS.clear()
+        w = I.workload(widx)
+        inp = I.make_prefill_inputs(w, per_mode=True)
+        _FULL_PM_INPUTS[widx] = (w, inp, device_inputs(inp))
+    w, inp, d = _FULL_PM_INPUTS[widx]
+    log(f"full size workload {w.name}, per-mode controls: GPU prefill K_T={K_T} Lc={w.Lc}")
+    y0 = torch.full_like(d["v"], 3.0)
+    call = essh.Prefill(d["v"], d["delta"], d["g_w"], d["g_r"], d["rho"], d["theta"], d["c"],
+                        K_T=K_T, Lc=w.Lc, y=y0)
+    y, st = call.run()
+    torch.cuda.synchronize()
+    call.check()
+    assert torch.all(y[:, :, K_T:] == 3.0), "channels past the tier were written"
+    rng = np.random.default_rng(2000 + 10 * widx + K_T)
+    samples = {(0, 0), (w.B - 1, K_T - 1), (int(rng.integers(w.B)), int(rng.integers(K_T)))}
+    tol = TOL[inp["io"]]
+    for b, k in sorted(samples):
+        sl = {key: (inp[key][b:b + 1, :, k:k + 1] if key in ("v", "delta", "g_w", "g_r") else
+                    inp[key][k:k + 1] if key in ("rho", "theta", "c") else inp[key]) for key in inp}
+        y_ref, s_ref = oracle.prefill(**oracle_inputs(sl))
+        yk = to_host_f64(y[b:b + 1, :, k:k + 1])
+        sk = to_host_f64(st[b:b + 1, k:k + 1])
+        ey, es = block_err(yk, y_ref, 2), block_err(sk, s_ref, 1)
+        log(f"  (b={b}, k={k}) L={w.L}: y err {ey:.3e}, state err {es:.3e}")
+        assert ey <= tol and es <= tol
+
+
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
