@@ -475,7 +475,7 @@ def test_prefill_full_size_sampled(widx, K_T):
 # bench.py times it, whose plans (segment lengths filling whole rounds of workgroups, whole
 # sequences at the 1.5B-class K_T = 32) no reduced shape reaches: sampled sequences against
 # the oracle, y and final state.
-FULL_PM = [(1, 24), (1, 12), (1, 6), (2, 8), (2, 32)]
+FULL_PM = [(1, 24), (1, 12), (1, 6), (2, 8), (2, 16), (2, 32)]
 _FULL_PM_INPUTS = {}
 
 
