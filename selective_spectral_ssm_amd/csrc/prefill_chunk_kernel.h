@@ -613,7 +613,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
         sm.psi[tau] = s;
     }
     lds_barrier();
-    if constexpr (PM) {
+    if constexpr (PM && !AGG) {   // tables of the output operands only
         for (int idx = tid; idx < 16 * M; idx += C::THREADS) {
             const int e = idx / M, j = idx - e * M;
             const float4 mt = sm.mtab[j];
@@ -983,7 +983,7 @@ prefill_chunk_kernel(PrefillArgs a, ScanPlan plan) {
                     if (t < LC) {
                         spm.q[j][t] = qv[u];
                         const float d = qv[u] - qp;   // >= 0 (log2 units)
-                        spm.fa[j][t] = exp2f(-d) * spm.gr[j][t];
+                        if constexpr (!AGG) spm.fa[j][t] = exp2f(-d) * spm.gr[j][t];   // output side only
                         spm.fb[j][t] = t < n ? exp2f(d) * spm.gw[j][t] : 0.f;
                         if (t == min(T0 + 15, n - 1)) spm.ftr[j][t >> 4] = exp2f(-d);
                     }
