@@ -472,9 +472,9 @@ def test_prefill_full_size_sampled(widx, K_T):
 
 
 # The per-mode control form (Eq. 5: clock and gates [B, L, K, m]) at the full sizes and tiers
-# bench.py times it, whose plans (segment lengths filling whole rounds of workgroups, whole
-# sequences at the 1.5B-class K_T = 32) no reduced shape reaches: sampled sequences against
-# the oracle, y and final state.
+# bench.py times it (and the 1.5B-class K_T = 16), whose plans (segment lengths filling whole
+# rounds of workgroups; whole sequences at the 1.5B-class K_T = 16 and 32) no reduced shape
+# reaches: sampled sequences against the oracle, y and final state.
 FULL_PM = [(1, 24), (1, 12), (1, 6), (2, 8), (2, 16), (2, 32)]
 _FULL_PM_INPUTS = {}
 
