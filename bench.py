@@ -371,7 +371,7 @@ def _lscpu_model():
 
 
 def cpu_baseline(inp, w, K_T, runs=5):
-    """The CPU oracle timed on this host, as the benchmark spec plans it: the oracle's C source built
+    """The CPU oracle timed on this host: the oracle's C source built
     as float32 with -O3 -march=native for this host, OpenMP over the independent (batch row,
     channel) sequences on every host core, median of `runs` runs after one warm-up; the same
     on one thread; and the decode step (24 layers) on all cores.  A reported baseline only."""
